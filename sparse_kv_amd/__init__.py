@@ -1,0 +1,381 @@
+"""sparse_kv_amd -- block-sparse long-context decode attention for AMD MI355X.
+
+Thin Python binding (ctypes) over the C ABI of ``libsparse_kv.so``
+(declared in include/sparse_kv.h).  Functions carry the C names and only
+marshal arguments: they check tensors, allocate outputs with torch when the
+caller passes none, and queue the HIP kernels on the current torch stream.
+Every step of the computation runs in the library's kernels; there is no
+fallback: the first call raises ImportError if the library has not been
+built (``python -m sparse_kv_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparse_kv.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_WORKSPACE = 0, -1, -2, -3, -4
+ATTN_F32, ATTN_BF16 = 0, 1
+BLOCK = 64
+
+EXPORTS = (
+    "attn_decode_dense",
+    "attn_merge_states",
+    "attn_build_centroids",
+    "attn_score_centroids",
+    "attn_select_topk",
+    "attn_decode_sparse",
+    "attn_decode_art",
+    "attn_decode_routed",
+    "attn_routed_workspace_bytes",
+    "attn_status_string",
+)
+
+
+class AttnDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+_D = ctypes.POINTER(AttnDims)
+_SIG = {
+    "attn_decode_dense": [_D, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
+    "attn_merge_states": [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P],
+    "attn_build_centroids": [_D, _P, _P, _P, _P],
+    "attn_score_centroids": [_D, _P, _P, _P, _P, _P],
+    "attn_select_topk": [_D, _P, _P, _I, _I, _I, _I, _P, _P, _P],
+    "attn_decode_sparse": [_D, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P],
+    "attn_decode_art": [_D, _P, _P, _P, _P, _P, _F, _F, _I, _I, _P, _P, _P, _P],
+    "attn_decode_routed": [_D, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _P, ctypes.c_size_t, _P, _P],
+    "attn_routed_workspace_bytes": [_D, _I, _I, _I],
+}
+_lib = None
+
+
+def lib():
+    """The loaded ctypes library; raises ImportError if it was never built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m sparse_kv_amd.build` (needs hipcc)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIG.items():
+            fn = getattr(h, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_size_t if name == "attn_routed_workspace_bytes" else ctypes.c_int
+        h.attn_status_string.argtypes = [ctypes.c_int]
+        h.attn_status_string.restype = ctypes.c_char_p
+        _lib = h
+    return _lib
+
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status == ATTN_OK:
+        return
+    msg = f"{what}: {attn_status_string(status)} (status {status})"
+    if status in (ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE):
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise ValueError(f"unsupported dtype {t.dtype}: q, k, v must be bfloat16 or float32")
+
+
+def _norm_dev(device):
+    d = torch.device(device)
+    if d.type == "cuda" and d.index is None:
+        d = torch.device("cuda", torch.cuda.current_device())
+    return d
+
+
+def _need(t, name, device, dtype=None, shape=None):
+    device = _norm_dev(device)
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _dims_from(q, k, scale=None):
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and k, v [B, Hkv, Lmax, d]")
+    B, Hq, d = q.shape
+    Bk, Hkv, Lmax, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree")
+    if Lmax % BLOCK != 0:
+        raise ValueError(f"KV length {Lmax} must be a multiple of the block size {BLOCK}")
+    if q.dtype != k.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    return AttnDims(B, Hq, Hkv, d, BLOCK, Lmax // BLOCK, _dtype_code(k), s)
+
+
+def _out(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _need(t, name, device, dtype, shape)
+
+
+def _seq(seq_lens, B, device):
+    if seq_lens is None:
+        return None
+    return _need(seq_lens, "seq_lens", device, torch.int32, (B,))
+
+
+def attn_decode_dense(q, k, v, seq_lens=None, num_splits=16, block_begin=0, block_end=-1,
+                      scale=None, m=None, l=None, o=None):
+    """Per-split softmax states (m, l, o) of decode attention over a block range."""
+    dev = q.device
+    dims = _dims_from(q, k, scale)
+    _need(q, "q", dev)
+    _need(k, "k", dev)
+    _need(v, "v", dev, k.dtype, k.shape)
+    seq = _seq(seq_lens, dims.batch, dev)
+    rows = (dims.batch, dims.num_q_heads, int(num_splits))
+    m = _out(m, rows, torch.float32, dev, "m")
+    l = _out(l, rows, torch.float32, dev, "l")
+    o = _out(o, rows + (dims.head_dim,), torch.float32, dev, "o")
+    with torch.cuda.device(dev):
+        st = lib().attn_decode_dense(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(seq),
+                                    int(block_begin), int(block_end), int(num_splits),
+                                    _ptr(m), _ptr(l), _ptr(o), _stream(dev))
+    _check(st, "attn_decode_dense")
+    return m, l, o
+
+
+def attn_merge_states(m, l, o, out=None, m_out=None, l_out=None):
+    """Merge the last split axis: m, l [..., S], o [..., S, d] -> out [..., d].
+
+    Returns out, or (out, m_out, l_out) when m_out / l_out are requested by
+    passing tensors or True.
+    """
+    dev = o.device
+    S, d = o.shape[-2], o.shape[-1]
+    lead = tuple(o.shape[:-2])
+    _need(o, "o", dev, torch.float32)
+    _need(m, "m", dev, torch.float32, lead + (S,))
+    _need(l, "l", dev, torch.float32, lead + (S,))
+    rows = int(math.prod(lead))
+    want_state = m_out is not None or l_out is not None
+    out = _out(out, lead + (d,), torch.float32, dev, "out")
+    if m_out is True or (want_state and m_out is None):
+        m_out = torch.empty(lead, dtype=torch.float32, device=dev)
+    if l_out is True or (want_state and l_out is None):
+        l_out = torch.empty(lead, dtype=torch.float32, device=dev)
+    if want_state:
+        _need(m_out, "m_out", dev, torch.float32, lead)
+        _need(l_out, "l_out", dev, torch.float32, lead)
+    with torch.cuda.device(dev):
+        st = lib().attn_merge_states(rows, S, d, _ptr(m), _ptr(l), _ptr(o), _ptr(out),
+                                    _ptr(m_out) if want_state else None,
+                                    _ptr(l_out) if want_state else None, _stream(dev))
+    _check(st, "attn_merge_states")
+    return (out, m_out, l_out) if want_state else out
+
+
+def attn_build_centroids(k, seq_lens=None, out=None, num_q_heads=None):
+    """Block-mean centroids [B, Hkv, NBmax, d] float32."""
+    dev = k.device
+    _need(k, "k", dev)
+    B, Hkv, Lmax, d = k.shape
+    if Lmax % BLOCK:
+        raise ValueError(f"KV length {Lmax} must be a multiple of {BLOCK}")
+    dims = AttnDims(B, num_q_heads or Hkv, Hkv, d, BLOCK, Lmax // BLOCK, _dtype_code(k), 1.0)
+    seq = _seq(seq_lens, B, dev)
+    out = _out(out, (B, Hkv, Lmax // BLOCK, d), torch.float32, dev, "out")
+    with torch.cuda.device(dev):
+        st = lib().attn_build_centroids(ctypes.byref(dims), _ptr(k), _ptr(seq), _ptr(out), _stream(dev))
+    _check(st, "attn_build_centroids")
+    return out
+
+
+def attn_score_centroids(q, centroids, seq_lens=None, scale=None, out=None):
+    """Group scores [B, Hkv, NBmax] float32 (-inf past each sequence's end)."""
+    dev = q.device
+    _need(q, "q", dev)
+    _need(centroids, "centroids", dev, torch.float32)
+    B, Hq, d = q.shape
+    Bc, Hkv, NBmax, dc = centroids.shape
+    if Bc != B or dc != d:
+        raise ValueError("q and centroids disagree")
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dims = AttnDims(B, Hq, Hkv, d, BLOCK, NBmax, _dtype_code(q), s)
+    seq = _seq(seq_lens, B, dev)
+    out = _out(out, (B, Hkv, NBmax), torch.float32, dev, "out")
+    with torch.cuda.device(dev):
+        st = lib().attn_score_centroids(ctypes.byref(dims), _ptr(q), _ptr(centroids), _ptr(seq),
+                                       _ptr(out), _stream(dev))
+    _check(st, "attn_score_centroids")
+    return out
+
+
+def attn_select_topk(scores, seq_lens=None, k=0, n_sink_blocks=1, n_recent_blocks=0, max_sel=None,
+                     block_idx=None, n_sel=None, shape=None, device=None):
+    """Chosen blocks (ascending, -1 padded) [B, Hkv, max_sel] and counts [B, Hkv].
+
+    scores [B, Hkv, NBmax] float32, or None with k == 0 and shape=(B, Hkv, NBmax).
+    """
+    if scores is not None:
+        dev = scores.device
+        _need(scores, "scores", dev, torch.float32)
+        B, Hkv, NBmax = scores.shape
+    else:
+        if k != 0 or shape is None:
+            raise ValueError("scores may only be omitted with k == 0 and an explicit shape")
+        B, Hkv, NBmax = shape
+        dev = _norm_dev(device) if device is not None else seq_lens.device
+    if max_sel is None:
+        max_sel = max(1, min(NBmax, int(n_sink_blocks) + int(n_recent_blocks) + int(k)))
+    dims = AttnDims(B, Hkv, Hkv, 64, BLOCK, NBmax, ATTN_F32, 1.0)
+    seq = _seq(seq_lens, B, dev)
+    block_idx = _out(block_idx, (B, Hkv, max_sel), torch.int32, dev, "block_idx")
+    n_sel = _out(n_sel, (B, Hkv), torch.int32, dev, "n_sel")
+    with torch.cuda.device(dev):
+        st = lib().attn_select_topk(ctypes.byref(dims), _ptr(scores), _ptr(seq), int(k), int(n_sink_blocks),
+                                   int(n_recent_blocks), int(max_sel), _ptr(block_idx), _ptr(n_sel),
+                                   _stream(dev))
+    _check(st, "attn_select_topk")
+    return block_idx, n_sel
+
+
+def attn_decode_sparse(q, k, v, block_idx, n_sel, seq_lens=None, num_splits=4, scale=None,
+                       m=None, l=None, o=None):
+    """Per-split states of attention over the listed blocks only."""
+    dev = q.device
+    dims = _dims_from(q, k, scale)
+    _need(q, "q", dev)
+    _need(k, "k", dev)
+    _need(v, "v", dev, k.dtype, k.shape)
+    _need(block_idx, "block_idx", dev, torch.int32)
+    if block_idx.dim() != 3 or tuple(block_idx.shape[:2]) != (dims.batch, dims.num_kv_heads):
+        raise ValueError("block_idx must be [B, Hkv, max_sel]")
+    _need(n_sel, "n_sel", dev, torch.int32, (dims.batch, dims.num_kv_heads))
+    seq = _seq(seq_lens, dims.batch, dev)
+    rows = (dims.batch, dims.num_q_heads, int(num_splits))
+    m = _out(m, rows, torch.float32, dev, "m")
+    l = _out(l, rows, torch.float32, dev, "l")
+    o = _out(o, rows + (dims.head_dim,), torch.float32, dev, "o")
+    with torch.cuda.device(dev):
+        st = lib().attn_decode_sparse(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(seq),
+                                     _ptr(block_idx), _ptr(n_sel), int(block_idx.shape[2]),
+                                     int(num_splits), _ptr(m), _ptr(l), _ptr(o), _stream(dev))
+    _check(st, "attn_decode_sparse")
+    return m, l, o
+
+
+def attn_decode_art(q, k, v, seq_lens=None, order=None, tau=1e-3, phi=1e-4, patience=2, probe_dim=8,
+                    scale=None, out=None, stop_pos=None, blocks_fetched=None):
+    """ART decode: (out [B, Hq, d] float32, stop_pos [B, Hq], blocks_fetched [B, Hkv])."""
+    dev = q.device
+    dims = _dims_from(q, k, scale)
+    _need(q, "q", dev)
+    _need(k, "k", dev)
+    _need(v, "v", dev, k.dtype, k.shape)
+    seq = _seq(seq_lens, dims.batch, dev)
+    if order is not None:
+        _need(order, "order", dev, torch.int32, (dims.batch, dims.num_kv_heads, dims.max_blocks))
+    out = _out(out, (dims.batch, dims.num_q_heads, dims.head_dim), torch.float32, dev, "out")
+    stop_pos = _out(stop_pos, (dims.batch, dims.num_q_heads), torch.int32, dev, "stop_pos")
+    blocks_fetched = _out(blocks_fetched, (dims.batch, dims.num_kv_heads), torch.int32, dev, "blocks_fetched")
+    with torch.cuda.device(dev):
+        st = lib().attn_decode_art(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(seq), _ptr(order),
+                                  float(tau), float(phi), int(patience), int(probe_dim), _ptr(out),
+                                  _ptr(stop_pos), _ptr(blocks_fetched), _stream(dev))
+    _check(st, "attn_decode_art")
+    return out, stop_pos, blocks_fetched
+
+
+def attn_routed_workspace_bytes(q, k, n_shards=8, splits_per_shard=4, sa_splits=4, scale=None):
+    dims = _dims_from(q, k, scale)
+    return int(lib().attn_routed_workspace_bytes(ctypes.byref(dims), int(n_shards), int(splits_per_shard),
+                                                int(sa_splits)))
+
+
+def attn_decode_routed(qs, ks, vs, route_mask, seq_lens=None, n_shards=8, splits_per_shard=4,
+                       sa_block_idx=None, sa_n_sel=None, sa_splits=4, workspace=None, outs=None,
+                       scale=None):
+    """One decode step of a layer stack under a per-layer hard route mask.
+
+    qs, ks, vs: per-layer tensors of one shape; route_mask: sequence of 0/1
+    (1 = full attention).  Returns the list of per-layer outputs [B, Hq, d].
+    """
+    n = len(qs)
+    if not (len(ks) == len(vs) == len(route_mask) == n):
+        raise ValueError("qs, ks, vs and route_mask must have one entry per layer")
+    if n == 0:
+        return []
+    dev = qs[0].device
+    dims = _dims_from(qs[0], ks[0], scale)
+    for i in range(n):
+        _need(qs[i], f"qs[{i}]", dev, qs[0].dtype, qs[0].shape)
+        _need(ks[i], f"ks[{i}]", dev, ks[0].dtype, ks[0].shape)
+        _need(vs[i], f"vs[{i}]", dev, ks[0].dtype, ks[0].shape)
+    seq = _seq(seq_lens, dims.batch, dev)
+    if outs is None:
+        outs = [torch.empty((dims.batch, dims.num_q_heads, dims.head_dim), dtype=torch.float32, device=dev)
+                for _ in range(n)]
+    for i, t in enumerate(outs):
+        _need(t, f"outs[{i}]", dev, torch.float32, (dims.batch, dims.num_q_heads, dims.head_dim))
+    need = int(lib().attn_routed_workspace_bytes(ctypes.byref(dims), int(n_shards), int(splits_per_shard),
+                                                int(sa_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", dev)
+    mask = (ctypes.c_uint8 * n)(*[1 if int(x) else 0 for x in route_mask])
+    arr = ctypes.c_void_p * n
+    qa = arr(*[t.data_ptr() for t in qs])
+    ka = arr(*[t.data_ptr() for t in ks])
+    va = arr(*[t.data_ptr() for t in vs])
+    oa = arr(*[t.data_ptr() for t in outs])
+    max_sel = int(sa_block_idx.shape[-1]) if sa_block_idx is not None else 0
+    with torch.cuda.device(dev):
+        st = lib().attn_decode_routed(ctypes.byref(dims), n, ctypes.cast(mask, _P), ctypes.cast(qa, _P),
+                                     ctypes.cast(ka, _P), ctypes.cast(va, _P), _ptr(seq), int(n_shards),
+                                     int(splits_per_shard), _ptr(sa_block_idx), _ptr(sa_n_sel), max_sel,
+                                     int(sa_splits), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), ctypes.cast(oa, _P),
+                                     _stream(dev))
+    _check(st, "attn_decode_routed")
+    return outs

@@ -1,0 +1,70 @@
+"""Build libsparse_kv.so (all HIP sources, gfx950) in-tree with hipcc.
+
+Usage: python -m sparse_kv_amd.build   (or call build()).
+Objects go to sparse_kv_amd/_build/, the library to sparse_kv_amd/libsparse_kv.so.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "csrc")
+INC = os.path.join(ROOT, "include")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libsparse_kv.so")
+SOURCES = ["api.hip", "decode.hip", "merge.hip", "select.hip", "art.hip"]
+ARCH = "gfx950"
+
+# Packed fp32 VALU ops are kept out of the generated code on purpose.
+CFLAGS = [
+    "-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INC, "-I", SRC,
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
+
+    def compile_one(i):
+        out = _run([cc, *CFLAGS, "-c", os.path.join(SRC, SOURCES[i]), "-o", objs[i]])
+        if verbose and out.strip():
+            print(out)
+
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(compile_one, range(len(SOURCES))))
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)

@@ -1,0 +1,278 @@
+// C ABI of the decode-attention library: argument checks and kernel dispatch.
+// Host code only; every kernel is queued on the caller's stream and nothing
+// here allocates, frees or synchronises.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+#include "sparse_kv.h"
+
+namespace {
+
+constexpr int32_t kMaxGrid = 65535;
+
+int check_dims(const attn_dims* d) {
+  if (!d) return ATTN_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->batch > kMaxGrid) return ATTN_ERR_INVALID_ARG;
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_kv_heads > kMaxGrid) return ATTN_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return ATTN_ERR_INVALID_ARG;
+  if (d->head_dim < 1 || d->block_size < 1 || d->max_blocks < 1) return ATTN_ERR_INVALID_ARG;
+  if (d->dtype != ATTN_F32 && d->dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (!isfinite(d->scale)) return ATTN_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d->block_size != 64) return ATTN_ERR_UNSUPPORTED;
+  if (d->num_q_heads / d->num_kv_heads > 8) return ATTN_ERR_UNSUPPORTED;
+  // one (b, kv head) slice of K or V must be addressable with 32-bit offsets
+  const uint64_t row_bytes = (uint64_t)d->head_dim * (d->dtype == ATTN_BF16 ? 2 : 4);
+  if ((uint64_t)d->max_blocks * 64 * row_bytes >= (1ull << 32)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+skv::DecodeArgs decode_args(const attn_dims* d, const void* q, const void* k, const void* v,
+                            const int32_t* seq_lens, int32_t S, float* m, float* l, float* o) {
+  skv::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.seq_lens = seq_lens;
+  a.m = m;
+  a.l = l;
+  a.o = o;
+  a.B = d->batch;
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.d = d->head_dim;
+  a.NBmax = d->max_blocks;
+  a.S = S;
+  a.block_begin = 0;
+  a.block_end = -1;
+  a.dtype = d->dtype;
+  a.scale = d->scale;
+  return a;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct RoutedLayout {
+  size_t m, l, o, sm, sl, so, total;  // byte offsets into the workspace
+};
+
+RoutedLayout routed_layout(const attn_dims* d, int32_t n_shards, int32_t sps, int32_t sa_splits) {
+  const size_t rows = (size_t)d->batch * d->num_q_heads;
+  const int64_t S = (int64_t)n_shards * sps;
+  const size_t Smax = (size_t)(S > sa_splits ? S : sa_splits);
+  RoutedLayout r{};
+  size_t off = 0;
+  r.m = off;
+  off += align256(rows * Smax * 4);
+  r.l = off;
+  off += align256(rows * Smax * 4);
+  r.o = off;
+  off += align256(rows * Smax * d->head_dim * 4);
+  r.sm = off;
+  off += align256(rows * n_shards * 4);
+  r.sl = off;
+  off += align256(rows * n_shards * 4);
+  r.so = off;
+  off += align256(rows * n_shards * d->head_dim * 4);
+  r.total = off;
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK:
+      return "ok";
+    case ATTN_ERR_INVALID_ARG:
+      return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED:
+      return "unsupported shape or dtype (head_dim must be 64 or 128, block_size 64, Hq/Hkv <= 8)";
+    case ATTN_ERR_HIP:
+      return "HIP launch or runtime error";
+    case ATTN_ERR_WORKSPACE:
+      return "workspace too small";
+    default:
+      return "unknown status";
+  }
+}
+
+int attn_decode_dense(const attn_dims* dims, const void* q, const void* k, const void* v,
+                      const int32_t* seq_lens, int32_t block_begin, int32_t block_end,
+                      int32_t num_splits, float* m, float* l, float* o, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !k || !v || !m || !l || !o) return ATTN_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > (1 << 24) || block_begin < 0) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  skv::DecodeArgs a = decode_args(dims, q, k, v, seq_lens, num_splits, m, l, o);
+  a.block_begin = block_begin;
+  a.block_end = block_end;
+  return hip_status(skv::launch_decode(a, false, (hipStream_t)stream));
+}
+
+int attn_merge_states(int32_t rows, int32_t num_splits, int32_t head_dim, const float* m,
+                      const float* l, const float* o, float* out, float* m_out, float* l_out,
+                      void* stream) {
+  if (rows < 0 || num_splits < 1) return ATTN_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return head_dim < 1 ? ATTN_ERR_INVALID_ARG : ATTN_ERR_UNSUPPORTED;
+  if (!m || !l || !o || !out) return ATTN_ERR_INVALID_ARG;
+  if (rows == 0) return ATTN_OK;
+  return hip_status(skv::launch_merge(rows, num_splits, head_dim, m, l, o, out, m_out, l_out,
+                                      (hipStream_t)stream));
+}
+
+int attn_build_centroids(const attn_dims* dims, const void* k, const int32_t* seq_lens,
+                         float* centroids, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!k || !centroids) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  return hip_status(skv::launch_build_centroids(k, seq_lens, centroids, dims->batch, dims->num_kv_heads,
+                                                dims->head_dim, dims->max_blocks, dims->dtype,
+                                                (hipStream_t)stream));
+}
+
+int attn_score_centroids(const attn_dims* dims, const void* q, const float* centroids,
+                         const int32_t* seq_lens, float* scores, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !centroids || !scores) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  return hip_status(skv::launch_score(q, centroids, seq_lens, scores, dims->batch, dims->num_q_heads,
+                                      dims->num_kv_heads, dims->head_dim, dims->max_blocks, dims->dtype,
+                                      dims->scale, (hipStream_t)stream));
+}
+
+int attn_select_topk(const attn_dims* dims, const float* scores, const int32_t* seq_lens,
+                     int32_t k, int32_t n_sink_blocks, int32_t n_recent_blocks, int32_t max_sel,
+                     int32_t* block_idx, int32_t* n_sel, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (k < 0 || n_sink_blocks < 0 || n_recent_blocks < 0 || max_sel < 1) return ATTN_ERR_INVALID_ARG;
+  if (!block_idx || !n_sel || (k > 0 && !scores)) return ATTN_ERR_INVALID_ARG;
+  const int64_t need = (int64_t)n_sink_blocks + n_recent_blocks + k;
+  if ((int64_t)max_sel < (need < dims->max_blocks ? need : (int64_t)dims->max_blocks)) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  return hip_status(skv::launch_topk(scores, seq_lens, dims->batch, dims->num_kv_heads, dims->max_blocks, k,
+                                     n_sink_blocks, n_recent_blocks, max_sel, block_idx, n_sel,
+                                     (hipStream_t)stream));
+}
+
+int attn_decode_sparse(const attn_dims* dims, const void* q, const void* k, const void* v,
+                       const int32_t* seq_lens, const int32_t* block_idx, const int32_t* n_sel,
+                       int32_t max_sel, int32_t num_splits, float* m, float* l, float* o,
+                       void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !k || !v || !block_idx || !n_sel || !m || !l || !o) return ATTN_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > (1 << 24) || max_sel < 1) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  skv::DecodeArgs a = decode_args(dims, q, k, v, seq_lens, num_splits, m, l, o);
+  a.block_idx = block_idx;
+  a.n_sel = n_sel;
+  a.max_sel = max_sel;
+  return hip_status(skv::launch_decode(a, true, (hipStream_t)stream));
+}
+
+int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const void* v,
+                    const int32_t* seq_lens, const int32_t* order, float tau, float phi,
+                    int32_t patience, int32_t probe_dim, float* out, int32_t* stop_pos,
+                    int32_t* blocks_fetched, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !k || !v || !out || !stop_pos) return ATTN_ERR_INVALID_ARG;
+  if (patience < 1 || probe_dim < 0 || isnan(tau) || isnan(phi)) return ATTN_ERR_INVALID_ARG;
+  if (probe_dim > 16 || probe_dim > dims->head_dim) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)dims->batch * dims->num_kv_heads > 0x7fffffff) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  skv::ArtArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.seq_lens = seq_lens;
+  a.order = order;
+  a.tau = tau;
+  a.phi = phi;
+  a.patience = patience;
+  a.probe_dim = probe_dim;
+  a.out = out;
+  a.stop_pos = stop_pos;
+  a.blocks_fetched = blocks_fetched;
+  a.B = dims->batch;
+  a.Hq = dims->num_q_heads;
+  a.Hkv = dims->num_kv_heads;
+  a.d = dims->head_dim;
+  a.NBmax = dims->max_blocks;
+  a.dtype = dims->dtype;
+  a.scale = dims->scale;
+  return hip_status(skv::launch_art(a, (hipStream_t)stream));
+}
+
+size_t attn_routed_workspace_bytes(const attn_dims* dims, int32_t n_shards, int32_t splits_per_shard,
+                                   int32_t sa_splits) {
+  if (check_dims(dims) != ATTN_OK || n_shards < 1 || splits_per_shard < 1 || sa_splits < 1) return 0;
+  return routed_layout(dims, n_shards, splits_per_shard, sa_splits).total;
+}
+
+int attn_decode_routed(const attn_dims* dims, int32_t n_layers, const uint8_t* route_mask,
+                       const void* const* q, const void* const* k, const void* const* v,
+                       const int32_t* seq_lens, int32_t n_shards, int32_t splits_per_shard,
+                       const int32_t* sa_block_idx, const int32_t* sa_n_sel, int32_t sa_max_sel,
+                       int32_t sa_splits, void* workspace, size_t workspace_bytes,
+                       float* const* out, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (n_layers < 0 || !route_mask || !q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
+  if (n_shards < 1 || splits_per_shard < 1 || sa_splits < 1) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)n_shards * splits_per_shard > (1 << 24)) return ATTN_ERR_INVALID_ARG;
+  bool any_sa = false;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    if (!q[i] || !k[i] || !v[i] || !out[i]) return ATTN_ERR_INVALID_ARG;
+    any_sa |= route_mask[i] == 0;
+  }
+  if (any_sa && (!sa_block_idx || !sa_n_sel || sa_max_sel < 1)) return ATTN_ERR_INVALID_ARG;
+  if (!workspace) return ATTN_ERR_INVALID_ARG;
+  const RoutedLayout lay = routed_layout(dims, n_shards, splits_per_shard, sa_splits);
+  if (workspace_bytes < lay.total) return ATTN_ERR_WORKSPACE;
+  if (dims->batch == 0 || n_layers == 0) return ATTN_OK;
+
+  char* ws = (char*)workspace;
+  float* m = (float*)(ws + lay.m);
+  float* l = (float*)(ws + lay.l);
+  float* o = (float*)(ws + lay.o);
+  float* sm = (float*)(ws + lay.sm);
+  float* sl = (float*)(ws + lay.sl);
+  float* so = (float*)(ws + lay.so);
+  const hipStream_t s = (hipStream_t)stream;
+  const int32_t rows = dims->batch * dims->num_q_heads;
+  const int32_t S = n_shards * splits_per_shard;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    hipError_t e;
+    if (route_mask[i]) {
+      // full attention: shard-aligned splits, merged per shard, then across shards
+      skv::DecodeArgs a = decode_args(dims, q[i], k[i], v[i], seq_lens, S, m, l, o);
+      e = skv::launch_decode(a, false, s);
+      if (e == hipSuccess)
+        e = skv::launch_merge(rows * n_shards, splits_per_shard, dims->head_dim, m, l, o, so, sm, sl, s);
+      if (e == hipSuccess) e = skv::launch_merge(rows, n_shards, dims->head_dim, sm, sl, so, out[i], nullptr, nullptr, s);
+    } else {
+      skv::DecodeArgs a = decode_args(dims, q[i], k[i], v[i], seq_lens, sa_splits, m, l, o);
+      a.block_idx = sa_block_idx;
+      a.n_sel = sa_n_sel;
+      a.max_sel = sa_max_sel;
+      e = skv::launch_decode(a, true, s);
+      if (e == hipSuccess) e = skv::launch_merge(rows, sa_splits, dims->head_dim, m, l, o, out[i], nullptr, nullptr, s);
+    }
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+}  // extern "C"

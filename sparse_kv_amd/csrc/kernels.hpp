@@ -1,0 +1,53 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;   // may be null: every row has NBmax * 64 tokens
+  const int32_t* block_idx;  // sparse only
+  const int32_t* n_sel;      // sparse only
+  int32_t max_sel;           // sparse only
+  float* m;
+  float* l;
+  float* o;
+  int32_t B, Hq, Hkv, d, NBmax, S, block_begin, block_end, dtype;
+  float scale;
+};
+
+struct ArtArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  const int32_t* order;  // may be null
+  float tau, phi;
+  int32_t patience, probe_dim;
+  float* out;
+  int32_t* stop_pos;
+  int32_t* blocks_fetched;  // may be null
+  int32_t B, Hq, Hkv, d, NBmax, dtype;
+  float scale;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, bool sparse, hipStream_t st);
+hipError_t launch_merge(int32_t rows, int32_t S, int32_t d, const float* m, const float* l,
+                        const float* o, float* out, float* m_out, float* l_out, hipStream_t st);
+hipError_t launch_build_centroids(const void* k, const int32_t* seq_lens, float* c, int32_t B,
+                                  int32_t Hkv, int32_t d, int32_t NBmax, int32_t dtype,
+                                  hipStream_t st);
+hipError_t launch_score(const void* q, const float* c, const int32_t* seq_lens, float* scores,
+                        int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t NBmax,
+                        int32_t dtype, float scale, hipStream_t st);
+hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int32_t B, int32_t Hkv,
+                       int32_t NBmax, int32_t k, int32_t n_sink, int32_t n_recent,
+                       int32_t max_sel, int32_t* idx, int32_t* n_sel, hipStream_t st);
+hipError_t launch_art(const ArtArgs& a, hipStream_t st);
+
+}  // namespace skv

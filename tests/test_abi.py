@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports what include/sparse_kv.h declares, and
+rejects bad host-visible arguments before queuing anything (CPU only: no
+call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_kv.h")
+
+
+@pytest.fixture(scope="module")
+def skv():
+    import sparse_kv_amd
+
+    if not os.path.exists(sparse_kv_amd.LIB_PATH):
+        from sparse_kv_amd import build
+
+        build.build()
+    sparse_kv_amd.lib()
+    return sparse_kv_amd
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\*?(attn_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(skv):
+    names = declared_functions()
+    assert len(names) >= 10, names
+    lib = ctypes.CDLL(skv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(skv.EXPORTS)
+
+
+def dims(**kw):
+    from sparse_kv_amd import AttnDims
+
+    d = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=64, max_blocks=4, dtype=1, scale=0.1)
+    d.update(kw)
+    return AttnDims(**d)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(head_dim=96), -2), (dict(head_dim=0), -1), (dict(block_size=32), -2),
+    (dict(num_q_heads=7), -1), (dict(num_q_heads=32, num_kv_heads=2), -2), (dict(dtype=5), -1),
+    (dict(max_blocks=0), -1), (dict(batch=-1), -1), (dict(scale=float("nan")), -1),
+    (dict(max_blocks=1 << 20), -2),
+])
+def test_dims_validation(skv, kw, expect):
+    lib = skv.lib()
+    d = dims(**kw)
+    st = lib.attn_decode_dense(ctypes.byref(d), FAKE, FAKE, FAKE, None, 0, -1, 4, FAKE, FAKE, FAKE, None)
+    assert st == expect
+
+
+def test_argument_validation(skv):
+    lib = skv.lib()
+    d = dims()
+    assert lib.attn_decode_dense(None, FAKE, FAKE, FAKE, None, 0, -1, 4, FAKE, FAKE, FAKE, None) == -1
+    assert lib.attn_decode_dense(ctypes.byref(d), None, FAKE, FAKE, None, 0, -1, 4, FAKE, FAKE, FAKE, None) == -1
+    assert lib.attn_decode_dense(ctypes.byref(d), FAKE, FAKE, FAKE, None, 0, -1, 0, FAKE, FAKE, FAKE, None) == -1
+    assert lib.attn_decode_dense(ctypes.byref(d), FAKE, FAKE, FAKE, None, -1, -1, 4, FAKE, FAKE, FAKE, None) == -1
+    assert lib.attn_merge_states(4, 0, 128, FAKE, FAKE, FAKE, FAKE, None, None, None) == -1
+    assert lib.attn_merge_states(4, 2, 96, FAKE, FAKE, FAKE, FAKE, None, None, None) == -2
+    assert lib.attn_merge_states(4, 2, 128, None, FAKE, FAKE, FAKE, None, None, None) == -1
+    # top-k: k > 0 needs scores; max_sel must hold the forced blocks plus k
+    assert lib.attn_select_topk(ctypes.byref(d), None, None, 2, 1, 1, 4, FAKE, FAKE, None) == -1
+    assert lib.attn_select_topk(ctypes.byref(d), FAKE, None, 2, 1, 1, 3, FAKE, FAKE, None) == -1
+    assert lib.attn_select_topk(ctypes.byref(d), FAKE, None, -1, 1, 1, 4, FAKE, FAKE, None) == -1
+    assert lib.attn_decode_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, 4, 2, FAKE, FAKE, FAKE,
+                                  None) == -1
+    # ART: patience >= 1, probe_dim in [0, 16], thresholds not NaN
+    args = [FAKE, FAKE, FAKE, None, None]
+    assert lib.attn_decode_art(ctypes.byref(d), *args, 1e-3, 1e-4, 0, 8, FAKE, FAKE, None, None) == -1
+    assert lib.attn_decode_art(ctypes.byref(d), *args, 1e-3, 1e-4, 2, -1, FAKE, FAKE, None, None) == -1
+    assert lib.attn_decode_art(ctypes.byref(d), *args, 1e-3, 1e-4, 2, 17, FAKE, FAKE, None, None) == -2
+    assert lib.attn_decode_art(ctypes.byref(d), *args, float("nan"), 1e-4, 2, 8, FAKE, FAKE, None, None) == -1
+    assert lib.attn_decode_art(ctypes.byref(d), *args, 1e-3, 1e-4, 2, 8, None, FAKE, None, None) == -1
+    # empty batch is a no-op success
+    d0 = dims(batch=0)
+    assert lib.attn_decode_dense(ctypes.byref(d0), FAKE, FAKE, FAKE, None, 0, -1, 4, FAKE, FAKE, FAKE, None) == 0
+
+
+def test_routed_workspace_and_validation(skv):
+    lib = skv.lib()
+    d = dims()
+    small = lib.attn_routed_workspace_bytes(ctypes.byref(d), 8, 2, 4)
+    big = lib.attn_routed_workspace_bytes(ctypes.byref(d), 8, 4, 4)
+    assert 0 < small < big
+    assert lib.attn_routed_workspace_bytes(ctypes.byref(d), 0, 2, 4) == 0
+    assert lib.attn_routed_workspace_bytes(ctypes.byref(dims(head_dim=96)), 8, 2, 4) == 0
+    mask = (ctypes.c_uint8 * 2)(1, 0)
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x1000)
+    P = ctypes.c_void_p
+    call = lambda ws_bytes, sa=FAKE: lib.attn_decode_routed(
+        ctypes.byref(d), 2, ctypes.cast(mask, P), ctypes.cast(ptrs, P), ctypes.cast(ptrs, P), ctypes.cast(ptrs, P),
+        None, 8, 2, sa, FAKE, 4, 4, FAKE, ws_bytes, ctypes.cast(ptrs, P), None)
+    assert call(small - 1) == -4
+    assert call(small, sa=None) == -1  # a sparse layer needs its block list
+
+
+def test_status_strings(skv):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(skv.attn_status_string(code), str) and skv.attn_status_string(code)

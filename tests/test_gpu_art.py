@@ -1,0 +1,121 @@
+"""GPU parity: ART early-terminated decode (exact stop positions)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.art import art_margin_ok
+from tests.gpu_util import TOL, assert_close, log, upload
+
+pytestmark = pytest.mark.gpu
+
+TAU, PHI, P, PROBE = 1e-3, 1e-4, 2, 8
+
+
+def art_inputs(cfg, B, Hq, Hkv, d, L, seq=None, dtype="bf16", recent=64 * 8, boost=12.0, order=None,
+               tau=TAU, phi=PHI, p=P, probe=PROBE):
+    """Recency-boosted inputs whose every ART decision clears a 1% band (units redrawn)."""
+    attempts = {}
+    G = Hq // Hkv
+    for _ in range(30):
+        inp = synth.make_inputs(cfg, B, Hq, Hkv, d, L, dtype=dtype, kind="recency", seq_lens=seq,
+                                attempts=attempts, recent_tokens=recent, boost=boost)
+        qf, kf, vf = inp.f64()
+        out, stop, traces = oracle.art_decode(qf, kf, vf, inp.seq_lens, inp.scale, tau, phi, p, probe, order=order)
+        bad = sorted({(b, h // G) for (b, h), tr in traces.items() if not art_margin_ok(tr, tau, phi)})
+        if not bad:
+            return inp, out, stop
+        for u in bad:
+            attempts[u] = attempts.get(u, 0) + 1
+    raise AssertionError("could not draw inputs with ART decision margins")
+
+
+def run_art(inp, order=None, tau=TAU, phi=PHI, p=P, probe=PROBE):
+    import sparse_kv_amd as skv
+
+    q, k, v, sl = upload(inp)
+    o = None if order is None else torch.from_numpy(np.ascontiguousarray(order, dtype=np.int32)).cuda()
+    out, stop, fetched = skv.attn_decode_art(q, k, v, sl, order=o, tau=tau, phi=phi, patience=p, probe_dim=probe)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), stop.cpu().numpy(), fetched.cpu().numpy()
+
+
+def check_fetched(fetched, stop, inp):
+    B, Hq, Hkv, _, _ = inp.shape
+    G = Hq // Hkv
+    for b in range(B):
+        nb = -(-int(inp.seq_lens[b]) // 64)
+        for g in range(Hkv):
+            need = int(stop[b, g * G:(g + 1) * G].max()) + 1
+            assert need <= fetched[b, g] <= min(nb, need + 7), (b, g, need, fetched[b, g])
+
+
+@pytest.mark.parametrize("label,B,Hq,Hkv,d,L,seq,dt", [
+    ("bf16-g4-d128", 2, 8, 2, 128, 64 * 48, [64 * 48, 64 * 40 + 17], "bf16"),
+    ("bf16-g4-d64", 2, 8, 2, 64, 64 * 40, None, "bf16"),
+    ("f32-g1-d64", 1, 2, 2, 64, 64 * 30, None, "f32"),
+    ("bf16-g8-d128", 1, 8, 1, 128, 64 * 36, None, "bf16"),
+])
+def test_art_stop_positions_exact(label, B, Hq, Hkv, d, L, seq, dt):
+    log(f"[art] {label}")
+    inp, ref_out, ref_stop = art_inputs(40, B, Hq, Hkv, d, L, seq=seq, dtype=dt)
+    out, stop, fetched = run_art(inp)
+    log(f"  stops {ref_stop.ravel().tolist()}")
+    assert np.array_equal(stop, ref_stop), (stop, ref_stop)
+    assert_close(out, ref_out, TOL, "ART output")
+    check_fetched(fetched, stop, inp)
+    assert (ref_stop < np.array([-(-int(s) // 64) for s in inp.seq_lens])[:, None] - 1).any(), \
+        "the case should stop early somewhere"
+
+
+def test_art_special_cases_reduce_to_dense():
+    log("[art] tau = phi = 0, probe off, patience > nb, tau = phi = inf")
+    inp = synth.make_inputs(41, 2, 8, 2, 128, 64 * 20, kind="recency", seq_lens=[64 * 20, 64 * 11 + 5],
+                            recent_tokens=64 * 4)
+    qf, kf, vf = inp.f64()
+    dense = oracle.decode_dense(qf, kf, vf, inp.seq_lens, inp.scale)
+    nbs = np.array([20, 12])[:, None]
+    for tau, phi, p, probe in ((0.0, 0.0, 1, 8), (1.0, 1.0, 2, 0), (math.inf, math.inf, 30, 8)):
+        out, stop, fetched = run_art(inp, tau=tau, phi=phi, p=p, probe=probe)
+        assert (stop == nbs - 1).all(), (tau, phi, p, probe, stop)
+        assert (fetched == nbs).all()
+        assert_close(out, dense, TOL, f"dense-equivalent ART tau={tau} probe={probe}")
+    out, stop, fetched = run_art(inp, tau=math.inf, phi=math.inf, p=1, probe=8)
+    assert (stop == 1).all()
+    ref_out, ref_stop, _ = oracle.art_decode(qf, kf, vf, inp.seq_lens, inp.scale, math.inf, math.inf, 1, 8)
+    assert_close(out, ref_out, TOL, "stop after two blocks")
+
+
+def test_art_custom_visit_order():
+    log("[art] custom visit orders starting with block 0")
+    B, Hq, Hkv, L = 1, 8, 2, 64 * 24
+    nb = 24
+    r = np.random.default_rng(3)
+    order = np.zeros((B, Hkv, nb), dtype=np.int32)
+    for g in range(Hkv):
+        order[0, g] = [0] + list(r.permutation(np.arange(1, nb)))
+    inp = synth.make_inputs(42, B, Hq, Hkv, 128, L, kind="recency", recent_tokens=64 * 6)
+    qf, kf, vf = inp.f64()
+    out, stop, _ = run_art(inp, order=order, tau=0.0, phi=0.0)
+    assert (stop == nb - 1).all()
+    assert_close(out, oracle.decode_dense(qf, kf, vf, inp.seq_lens, inp.scale), TOL, "order-invariant dense")
+    inp, ref_out, ref_stop = art_inputs(43, B, Hq, Hkv, 128, L, recent=64 * 6, order=order)
+    out, stop, _ = run_art(inp, order=order)
+    assert np.array_equal(stop, ref_stop)
+    assert_close(out, ref_out, TOL, "custom-order ART output")
+
+
+def test_art_empty_and_single_block_rows():
+    log("[art] rows with 0 and 1 blocks")
+    inp = synth.make_inputs(44, 3, 4, 1, 128, 64 * 4, kind="gauss", seq_lens=[0, 30, 64 * 4])
+    out, stop, fetched = run_art(inp)
+    qf, kf, vf = inp.f64()
+    ref_out, ref_stop, _ = oracle.art_decode(qf, kf, vf, inp.seq_lens, inp.scale, TAU, PHI, P, PROBE)
+    assert stop[0].tolist() == [-1] * 4 and not out[0].any() and fetched[0, 0] == 0
+    assert stop[1].tolist() == [0] * 4 and fetched[1, 0] == 1
+    assert np.array_equal(stop, ref_stop)
+    assert_close(out, ref_out, TOL, "output")

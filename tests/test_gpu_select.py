@@ -1,0 +1,178 @@
+"""GPU parity: centroids, scores, top-k selection and listed-block decode."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.selection import selection_gap
+from tests.gpu_util import TOL, assert_close, assert_states_close, log, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dt,d,seq", [("bf16", 128, [64 * 21, 64 * 7 + 9]), ("f32", 64, [64 * 21, 1]),
+                                     ("bf16", 64, [0, 64 * 21]), ("f32", 128, [64 * 21, 64 * 3])])
+def test_centroids_and_scores(dt, d, seq):
+    log(f"[select] centroids + scores {dt} d={d} seq={seq}")
+    inp = synth.make_inputs(30, 2, 8, 2, d, 64 * 21, dtype=dt, kind="mixture", seq_lens=seq)
+    q, k, v, sl = upload(inp)
+    import sparse_kv_amd as skv
+
+    C = skv.attn_build_centroids(k, sl)
+    sc = skv.attn_score_centroids(q, C, sl)
+    torch.cuda.synchronize()
+    qf, kf, _ = inp.f64()
+    RC = oracle.block_centroids(kf, inp.seq_lens)
+    assert_close(C.cpu().numpy(), RC, 1e-5, "centroids")
+    RS = oracle.centroid_scores(qf, RC, inp.seq_lens, inp.scale)
+    got = sc.cpu().numpy()
+    assert np.array_equal(np.isneginf(got), np.isneginf(RS)), "-inf pattern past the end"
+    fin = np.isfinite(RS)
+    assert_close(got[fin], RS[fin], 1e-4, "scores")
+
+
+def upload_scores(s):
+    return torch.from_numpy(np.ascontiguousarray(s, dtype=np.float32)).cuda()
+
+
+@pytest.mark.parametrize("k,ns,nr", [(3, 1, 2), (0, 1, 4), (50, 1, 1), (5, 0, 0), (2, 3, 40), (1, 0, 0)])
+def test_topk_exact_on_given_scores(k, ns, nr):
+    log(f"[select] top-k k={k} sink={ns} recent={nr}")
+    r = np.random.default_rng(k * 100 + ns * 10 + nr)
+    B, Hkv, NB = 4, 3, 33
+    s = r.standard_normal((B, Hkv, NB)).astype(np.float32)
+    s[1, 2, 5:15] = 0.25  # a run of exact ties
+    s[2, 0, :] = 1.0  # everything tied
+    s[3, 1, 4] = -0.0
+    s[3, 1, 9] = 0.0
+    seq = np.array([64 * NB, 64 * 10 + 1, 64, 0], dtype=np.int32)
+    import sparse_kv_amd as skv
+
+    max_sel = min(NB, ns + nr + k) + 2
+    idx, n = skv.attn_select_topk(upload_scores(s) if k > 0 else None, torch.from_numpy(seq).cuda(), k=k,
+                                  n_sink_blocks=ns, n_recent_blocks=nr, max_sel=max_sel,
+                                  shape=(B, Hkv, NB), device="cuda")
+    torch.cuda.synchronize()
+    idx, n = idx.cpu().numpy(), n.cpu().numpy()
+    ref = oracle.select_all(s.astype(np.float64), seq, k, ns, nr)
+    for b in range(B):
+        for g in range(Hkv):
+            want = ref[b][g]
+            assert n[b, g] == len(want), (b, g, n[b, g], want)
+            assert idx[b, g, :len(want)].tolist() == want, (b, g)
+            assert (idx[b, g, len(want):] == -1).all()
+
+
+def test_topk_large_rows_radix_paths():
+    log("[select] top-k on 4096-block rows")
+    r = np.random.default_rng(9)
+    B, Hkv, NB = 2, 2, 4096
+    s = (r.standard_normal((B, Hkv, NB)) * 3).astype(np.float32)
+    s[0, 1] = np.round(s[0, 1] * 4) / 4  # heavy ties
+    s[1, 0, 100:200] = s[1, 0, 3000]  # ties at the boundary region
+    seq = np.array([64 * NB, 64 * 3000 - 17], dtype=np.int32)
+    import sparse_kv_amd as skv
+
+    for k, ns, nr in ((410, 1, 64), (1, 1, 0), (3000, 2, 7)):
+        idx, n = skv.attn_select_topk(upload_scores(s), torch.from_numpy(seq).cuda(), k=k, n_sink_blocks=ns,
+                                      n_recent_blocks=nr)
+        torch.cuda.synchronize()
+        idx, n = idx.cpu().numpy(), n.cpu().numpy()
+        ref = oracle.select_all(s.astype(np.float64), seq, k, ns, nr)
+        for b in range(B):
+            for g in range(Hkv):
+                assert idx[b, g, :n[b, g]].tolist() == ref[b][g], (k, b, g)
+
+
+def margin_inputs(cfg, B, Hq, Hkv, d, L, k, ns, nr, seq=None, **kw):
+    """Mixture inputs whose top-k boundary clears a 1e-4 score gap (units redrawn)."""
+    attempts = {}
+    for _ in range(20):
+        inp = synth.make_inputs(cfg, B, Hq, Hkv, d, L, kind="mixture", seq_lens=seq, attempts=attempts, **kw)
+        qf, kf, _ = inp.f64()
+        sig = oracle.centroid_scores(qf, oracle.block_centroids(kf, inp.seq_lens), inp.seq_lens, inp.scale)
+        bad = []
+        for b in range(B):
+            nb = -(-int(inp.seq_lens[b]) // 64)
+            for g in range(Hkv):
+                if selection_gap(sig[b, g], nb, k, ns, nr) <= 1e-4:
+                    bad.append((b, g))
+        if not bad:
+            return inp, sig
+        for u in bad:
+            attempts[u] = attempts.get(u, 0) + 1
+    raise AssertionError("could not draw inputs with a selection margin")
+
+
+def test_selection_pipeline_and_sparse_decode_with_poison():
+    log("[select] centroid -> score -> top-k -> sparse decode, unselected blocks poisoned")
+    B, Hq, Hkv, d, L = 2, 8, 2, 128, 64 * 200
+    k, ns, nr = 20, 1, 6
+    inp, sig = margin_inputs(31, B, Hq, Hkv, d, L, k, ns, nr, seq=[64 * 200, 64 * 150 + 30])
+    q, kk, v, sl = upload(inp)
+    import sparse_kv_amd as skv
+
+    C = skv.attn_build_centroids(kk, sl)
+    sc = skv.attn_score_centroids(q, C, sl)
+    idx, n = skv.attn_select_topk(sc, sl, k=k, n_sink_blocks=ns, n_recent_blocks=nr)
+    torch.cuda.synchronize()
+    ref = oracle.select_all(sig, inp.seq_lens, k, ns, nr)
+    idx_np, n_np = idx.cpu().numpy(), n.cpu().numpy()
+    for b in range(B):
+        for g in range(Hkv):
+            assert idx_np[b, g, :n_np[b, g]].tolist() == ref[b][g], (b, g)
+    qf, kf, vf = inp.f64()
+    want = oracle.decode_blocks(qf, kf, vf, inp.seq_lens, inp.scale, ref)
+    synth.poison_blocks(inp, ref)
+    _, kp, vp, _ = upload(inp)
+    for S in (1, 3, 8):
+        m, l, o = skv.attn_decode_sparse(q, kp, vp, idx, n, sl, num_splits=S)
+        out = skv.attn_merge_states(m, l, o)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), want, TOL, f"sparse output S={S}")
+    rm, rl, ro = oracle.decode_sparse_split_states(qf, kf, vf, inp.seq_lens, inp.scale, ref, 3)
+    m, l, o = skv.attn_decode_sparse(q, kp, vp, idx, n, sl, num_splits=3)
+    torch.cuda.synchronize()
+    assert_states_close(m, l, o, rm, rl, ro, TOL, "sparse split states")
+
+
+def test_selecting_everything_equals_dense():
+    log("[select] k >= candidates gives dense attention")
+    inp = synth.make_inputs(32, 2, 8, 2, 128, 64 * 16, kind="gauss", seq_lens=[64 * 16, 64 * 9 + 1])
+    q, k, v, sl = upload(inp)
+    import sparse_kv_amd as skv
+
+    sc = skv.attn_score_centroids(q, skv.attn_build_centroids(k, sl), sl)
+    idx, n = skv.attn_select_topk(sc, sl, k=100, n_sink_blocks=1, n_recent_blocks=0)
+    out = skv.attn_merge_states(*skv.attn_decode_sparse(q, k, v, idx, n, sl, num_splits=4))
+    dense = skv.attn_merge_states(*skv.attn_decode_dense(q, k, v, sl, num_splits=4))
+    torch.cuda.synchronize()
+    assert n.cpu().tolist() == [[16, 16], [10, 10]]
+    assert_close(out.cpu().numpy(), dense.cpu().numpy(), 1e-5, "sparse(all) vs dense")
+
+
+def test_squeezed_worked_example_on_gpu():
+    # Squeezed Attention blog, Q1 worked example, embedded at d = 64 with
+    # 64-token blocks: block 0 holds keys like A-C, block 1 keys like D-F.
+    log("[select] worked example: the query picks the closer centroid")
+    r = np.random.default_rng(2)
+    d = 64
+    e1, e2 = np.eye(d)[0], np.eye(d)[1]
+    K = np.concatenate([e1 * 4 + 0.1 * r.standard_normal((64, d)), e2 * 4 + 0.1 * r.standard_normal((64, d))])
+    V = r.standard_normal((128, d))
+    qv = e2 * 2 + 0.05 * r.standard_normal(d)
+    t = lambda a: torch.from_numpy(a.astype(np.float32)).cuda()
+    q, k, v = t(qv[None, None]), t(K[None, None]), t(V[None, None])
+    import sparse_kv_amd as skv
+
+    sc = skv.attn_score_centroids(q, skv.attn_build_centroids(k))
+    idx, n = skv.attn_select_topk(sc, None, k=1, n_sink_blocks=0, n_recent_blocks=0)
+    out = skv.attn_merge_states(*skv.attn_decode_sparse(q, k, v, idx, n, None, num_splits=1))
+    torch.cuda.synchronize()
+    assert idx.cpu().tolist() == [[[1]]]
+    Kf, Vf, qf = K.astype(np.float32).astype(np.float64), V.astype(np.float32).astype(np.float64), qv.astype(
+        np.float32).astype(np.float64)
+    want = oracle.decode_blocks(qf[None, None], Kf[None, None], Vf[None, None], np.array([128]), 1 / 8.0, [[[1]]])
+    assert_close(out.cpu().numpy(), want, 1e-5, "cluster-2-only output")
