@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+Workload: one decode step of a Llama-3.1-8B-shaped attention layer at 128K
+context, batch 8 (32 query heads, 8 KV heads, head_dim 128, bf16 KV in 64-token
+blocks; keys a block-coherent Gaussian mixture, seeded synthetic data).
+
+One timed step runs every stage of the hot path over that batch:
+  dense   split-KV decode + merge over all 2048 blocks      (full attention)
+  sparse  centroid scores + top-k (10% + sink + last 64) + listed-block decode + merge
+  art     ART early-terminated decode, block 0 then most recent first
+  window  sink + recent-window decode + merge                 (routed SA layer)
+Block centroids are built once before timing (they change only when a block
+fills).  Each stage reads its own copy of the KV cache so that no stage is
+served from the 256 MB last-level cache filled by the previous one.
+
+value = algorithmic HBM bytes of the step / step time (GB/s).  The roofline
+object reports the dense decode kernel alone: its algorithmic bytes per launch
+over its average launch time, from HIP events on the launch stream.  The CPU
+baseline times the float64 oracle on a sample of (batch row, KV head) units.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attention HBM GB/s (% of peak) + tokens/sec at 128K ctx, batch 8"
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--splits", type=int, default=16, help="splits per (batch row, KV head), dense stage")
+    ap.add_argument("--sparse-splits", type=int, default=12, help="splits per unit, sparse stage")
+    ap.add_argument("--window-splits", type=int, default=4, help="splits per unit, sink+window stage")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stages", default="dense,sparse,art,window")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path is single-device; see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_kv_amd as skv
+    import synth
+
+    stages = [s for s in args.stages.split(",") if s]
+    W = synth.WORKLOADS[3]
+    B, Hq, Hkv, d, L = W["B"], W["Hq"], W["Hkv"], W["d"], W["L"]
+    NB = L // 64
+    topk, n_sink, n_recent = W["topk"], W["n_sink"], W["n_recent"]
+    win_recent = 128
+    tau, phi, patience, probe = 1e-3, 1e-4, 2, 8
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(3, B, Hq, Hkv, d, L, dtype="bf16", kind="mixture")
+    gen_s = time.perf_counter() - t0
+    print(f"[bench] generated 128K batch-8 inputs in {gen_s:.1f}s", file=sys.stderr, flush=True)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q = up(inp.q)
+    copies = {}
+    k0, v0 = up(inp.k), up(inp.v)
+    for i, s in enumerate(("dense", "sparse", "art", "window")):
+        copies[s] = (k0, v0) if i == 0 else (k0.clone(), v0.clone())
+    torch.cuda.synchronize()
+
+    # prefill-time work: centroids of the sparse stage's cache, the window list
+    c_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    c_ev[0].record()
+    C = skv.attn_build_centroids(copies["sparse"][0])
+    c_ev[1].record()
+    win_idx, win_n = skv.attn_select_topk(None, None, k=0, n_sink_blocks=n_sink, n_recent_blocks=win_recent,
+                                          shape=(B, Hkv, NB), device=dev)
+    torch.cuda.synchronize()
+    centroid_ms = c_ev[0].elapsed_time(c_ev[1])
+
+    f32 = dict(dtype=torch.float32, device=dev)
+    S, Ss, Sw = args.splits, args.sparse_splits, args.window_splits
+    st_d = (torch.empty((B, Hq, S), **f32), torch.empty((B, Hq, S), **f32), torch.empty((B, Hq, S, d), **f32))
+    st_s = (torch.empty((B, Hq, Ss), **f32), torch.empty((B, Hq, Ss), **f32), torch.empty((B, Hq, Ss, d), **f32))
+    st_w = (torch.empty((B, Hq, Sw), **f32), torch.empty((B, Hq, Sw), **f32), torch.empty((B, Hq, Sw, d), **f32))
+    out_d, out_s, out_w, out_a = (torch.empty((B, Hq, d), **f32) for _ in range(4))
+    scores = torch.empty((B, Hkv, NB), **f32)
+    max_sel = n_sink + n_recent + topk
+    sel_idx = torch.empty((B, Hkv, max_sel), dtype=torch.int32, device=dev)
+    sel_n = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    stop = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    fetched = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+
+    names = ["dense_kernel", "dense_merge", "sparse", "art", "window"]
+    ev = {}
+
+    def step(record):
+        def mark(tag):
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                ev.setdefault(tag, []).append(e)
+
+        if "dense" in stages:
+            kd, vd = copies["dense"]
+            mark("dense_kernel.0")
+            skv.attn_decode_dense(q, kd, vd, None, num_splits=S, m=st_d[0], l=st_d[1], o=st_d[2])
+            mark("dense_kernel.1")
+            skv.attn_merge_states(*st_d, out=out_d)
+            mark("dense_merge.1")
+        if "sparse" in stages:
+            ks, vs = copies["sparse"]
+            mark("sparse.0")
+            skv.attn_score_centroids(q, C, None, out=scores)
+            skv.attn_select_topk(scores, None, k=topk, n_sink_blocks=n_sink, n_recent_blocks=n_recent,
+                                 max_sel=max_sel, block_idx=sel_idx, n_sel=sel_n)
+            skv.attn_decode_sparse(q, ks, vs, sel_idx, sel_n, None, num_splits=Ss, m=st_s[0], l=st_s[1], o=st_s[2])
+            skv.attn_merge_states(*st_s, out=out_s)
+            mark("sparse.1")
+        if "art" in stages:
+            ka, va = copies["art"]
+            mark("art.0")
+            skv.attn_decode_art(q, ka, va, None, tau=tau, phi=phi, patience=patience, probe_dim=probe,
+                                out=out_a, stop_pos=stop, blocks_fetched=fetched)
+            mark("art.1")
+        if "window" in stages:
+            kw, vw = copies["window"]
+            mark("window.0")
+            skv.attn_decode_sparse(q, kw, vw, win_idx, win_n, None, num_splits=Sw, m=st_w[0], l=st_w[1], o=st_w[2])
+            skv.attn_merge_states(*st_w, out=out_w)
+            mark("window.1")
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+
+    def avg_ms(a, b):
+        xs = [e0.elapsed_time(e1) for e0, e1 in zip(ev[a], ev[b])]
+        return sum(xs) / len(xs)
+
+    # algorithmic bytes per stage
+    kv_block = 64 * d * 2 * 2  # K + V bytes of one block of one KV head
+    q_bytes = B * Hq * d * 2
+    o_bytes = B * Hq * d * 4
+    units = B * Hkv
+    paths = {}
+    total_bytes = 0.0
+    gbs = lambda by, ms: by / (ms * 1e-3) / 1e9
+    if "dense" in stages:
+        kern_ms = avg_ms("dense_kernel.0", "dense_kernel.1")
+        path_ms = avg_ms("dense_kernel.0", "dense_merge.1")
+        by = units * NB * kv_block + q_bytes + o_bytes
+        total_bytes += by
+        paths["dense"] = dict(ms=path_ms, kernel_ms=kern_ms, bytes=by, gbs=gbs(by, path_ms),
+                              pct_peak=100 * gbs(by, path_ms) / PEAK_HBM_GBS, tokens_per_s=B / (path_ms * 1e-3),
+                              splits=S)
+    if "sparse" in stages:
+        n_sel = sel_n.cpu().numpy()
+        ms = avg_ms("sparse.0", "sparse.1")
+        by = float(n_sel.sum()) * kv_block + units * NB * d * 4 + units * NB * 4 * 2 + q_bytes + o_bytes
+        total_bytes += by
+        paths["sparse"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), blocks_per_unit=float(n_sel.mean()),
+                               tokens_per_s=B / (ms * 1e-3), splits=Ss)
+    if "art" in stages:
+        stp = stop.cpu().numpy().reshape(B, Hkv, Hq // Hkv)
+        need = stp.max(axis=2) + 1
+        ms = avg_ms("art.0", "art.1")
+        by = float(need.sum()) * kv_block + q_bytes + o_bytes
+        total_bytes += by
+        paths["art"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), mean_stop=float(stp.mean()),
+                            blocks_needed_per_unit=float(need.mean()),
+                            blocks_fetched_per_unit=float(fetched.cpu().numpy().mean()),
+                            tokens_per_s=B / (ms * 1e-3))
+    if "window" in stages:
+        ms = avg_ms("window.0", "window.1")
+        by = float(win_n.cpu().numpy().sum()) * kv_block + q_bytes + o_bytes
+        total_bytes += by
+        paths["window"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), tokens_per_s=B / (ms * 1e-3), splits=Sw)
+    if "dense" in paths:
+        for k_ in ("sparse", "art", "window"):
+            if k_ in paths:
+                paths[k_]["speedup_vs_dense"] = paths["dense"]["ms"] / paths[k_]["ms"]
+
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode step, 128K context, batch 8, 32 q / 8 kv heads, d 128, bf16 KV, "
+                               "64-token blocks; dense + centroid top-k sparse + ART + sink/window stages",
+                   "batch": B, "context": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "block": 64,
+                   "stages": stages, "parallelism": "single-gpu"},
+        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(paths["dense"]["tokens_per_s"], 1) if "dense" in paths else None,
+        "centroid_build_ms": round(centroid_ms, 4),
+        "paths": {k_: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v_.items()}
+                  for k_, v_ in paths.items()},
+    }
+    if "dense" in paths:
+        kb = units * NB * kv_block + q_bytes + B * Hq * S * (d + 2) * 4
+        ach = kb / (paths["dense"]["kernel_ms"] * 1e-3) / 1e9
+        res["roofline"] = {"kernel": "decode_kernel (split-KV dense)", "bound": "hbm", "achieved": round(ach, 1),
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                           "traffic": None, "bytes_per_launch": kb,
+                           "avg_launch_ms": round(paths["dense"]["kernel_ms"], 5)}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, topk, n_sink, n_recent, win_recent,
+                                           tau, phi, patience, probe, total_bytes / units)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(inp, budget_s, topk, n_sink, n_recent, win_recent, tau, phi, patience, probe, bytes_per_unit):
+    """Time the float64 oracle on whole (batch row, KV head) units of the same input."""
+    import numpy as np
+
+    import oracle
+    from oracle.selection import forced_blocks
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    B, Hq, Hkv, d, L = inp.shape
+    G = Hq // Hkv
+    done = 0
+    t0 = time.perf_counter()
+    for u in range(B * Hkv):
+        b, g = divmod(u, Hkv)
+        qf = inp.upcast(inp.q[b:b + 1, g * G:(g + 1) * G])
+        kf = inp.upcast(inp.k[b:b + 1, g:g + 1])
+        vf = inp.upcast(inp.v[b:b + 1, g:g + 1])
+        seq = inp.seq_lens[b:b + 1]
+        oracle.decode_dense(qf, kf, vf, seq, inp.scale)
+        sig = oracle.centroid_scores(qf, oracle.block_centroids(kf, seq), seq, inp.scale)
+        lists = oracle.select_all(sig, seq, topk, n_sink, n_recent)
+        oracle.decode_blocks(qf, kf, vf, seq, inp.scale, lists)
+        oracle.art_decode(qf, kf, vf, seq, inp.scale, tau, phi, patience, probe)
+        nb = -(-int(seq[0]) // 64)
+        oracle.decode_blocks(qf, kf, vf, seq, inp.scale, [[sorted(forced_blocks(nb, n_sink, win_recent))]])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(done * bytes_per_unit / el / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {B * Hkv} (batch row, KV head) units of the same input, every stage, "
+                      f"float64 numpy, {el:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

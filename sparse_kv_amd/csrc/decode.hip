@@ -21,6 +21,9 @@
 //     are re-read in the row layout used for V (lane%CPR = 16-byte chunk,
 //     lane/CPR = token phase; one wave-wide load covers whole rows), where
 //     P.V is accumulated in fp32 with VALU FMAs: P is never rounded to bf16.
+//   * V is read with streaming (non-temporal) loads, whole rows per
+//     instruction; K, whose MFMA layout covers half a 128-byte line per
+//     instruction, goes through L2 so the second half is an L2 hit.
 //   * Reads past the sequence end hit the buffer range limit and return
 //     zeros (the whole byte offset goes in the VGPR offset, which is what the
 //     range check covers); their logits are masked to -inf.
@@ -102,18 +105,34 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   float* pl = p_lds[w];
   const int32_t* list = SPARSE ? p.block_idx + unit * (size_t)p.max_sel : nullptr;
 
-  for (int pos = lo + w; pos < hi; pos += kWaves) {
-    const int j = SPARSE ? clampi(list[pos], 0, nb - 1) : pos;
+  // Software pipeline: the next block's K is requested as soon as this
+  // block's logits are formed, its V as soon as this block's P.V is done, so
+  // every wave keeps a block's worth of loads in flight while it computes.
+  u32x4 kr[4][KA];
+  u32x4 vr[CPR];
+  auto block_at = [&](int pos) { return SPARSE ? clampi(list[pos], 0, nb - 1) : pos; };
+  auto load_k = [&](int j) {
     const uint32_t soff = (uint32_t)j * kBlock * ROWB;
-
-    u32x4 kr[4][KA];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
       for (int a = 0; a < KA; ++a) kr[t4][a] = load16(krs, soff + kvo + t4 * 16 * ROWB + a * 64, 0);
-    u32x4 vr[CPR];
+  };
+  auto load_v = [&](int j) {
+    const uint32_t soff = (uint32_t)j * kBlock * ROWB;
 #pragma unroll
-    for (int i = 0; i < CPR; ++i) vr[i] = load16(vrs, soff + vvo + i * TPI * ROWB, 0);
+    for (int i = 0; i < CPR; ++i) vr[i] = load16_nt(vrs, soff + vvo + i * TPI * ROWB, 0);
+  };
+  int jn = 0;
+  if (lo + w < hi) {
+    jn = block_at(lo + w);
+    load_k(jn);
+    load_v(jn);
+  }
+
+  for (int pos = lo + w; pos < hi; pos += kWaves) {
+    const int j = jn;
+    const bool more = pos + kWaves < hi;
 
     // logits: sc[t4][r] = <q_{4r + kg}, k_{16 t4 + arow}>
     f32x4 sc[4];
@@ -131,6 +150,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
         }
       }
       sc[t4] = c;
+    }
+    if (more) {
+      jn = block_at(pos + kWaves);
+      load_k(jn);
     }
 
     const int nvalid = min(kBlock, L - j * kBlock);
@@ -202,6 +225,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[q][e] = fmaf(pq[q], vf[e], acc[q][e]);
     }
+    if (more) load_v(jn);
   }
 
   // wave state: l over the 16 lanes of each row, P.V over the token phases

@@ -26,6 +26,14 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
 }
 
+// Streaming (non-temporal) 16-byte load, for data read once in whole
+// 128-byte lines: it is not kept in L2, which lets HBM run closer to peak.
+// Loads that touch only part of a line per instruction must not use it: the
+// rest of the line would be fetched again by the next instruction.
+__device__ __forceinline__ u32x4 load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2 /* nt */);
+}
+
 __device__ __forceinline__ float load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
 }
@@ -35,6 +43,9 @@ __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x 
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// Hardware reciprocal and reciprocal square root (about 1 ulp).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void centroid_kernel(const void* __restrict__ 
   for (int e = 0; e < E; ++e) sum[e] = 0.f;
 #pragma unroll
   for (int i = 0; i < CPR; ++i) {
-    const u32x4 x = load16(rs, base + i * TPI * ROWB, 0);
+    const u32x4 x = load16_nt(rs, base + i * TPI * ROWB, 0);
     if constexpr (BF) {
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void score_kernel(const void* __restrict__ q, 
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int j = j0 + it * RPI + lane / LPR;
-    const u32x4 x = load16(rs, ((uint32_t)j * D + 4 * c) * 4, 0);
+    const u32x4 x = load16_nt(rs, ((uint32_t)j * D + 4 * c) * 4, 0);
     float s = qs[0] * __uint_as_float(x[0]);
     s = fmaf(qs[1], __uint_as_float(x[1]), s);
     s = fmaf(qs[2], __uint_as_float(x[2]), s);
