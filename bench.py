@@ -33,6 +33,30 @@ if ROOT not in sys.path:
 
 METRIC = "decode attention HBM GB/s (% of peak) + tokens/sec at 128K ctx, batch 8"
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_decode128k_b8.md")
+DENSE_SOURCES = ("decode.hip", "device_common.hpp", "kernels.hpp")
+
+
+def measured_dense_traffic():
+    """HBM bytes per dense-kernel launch from the committed counter summary,
+    or None when the kernel sources changed since the counters were taken."""
+    import hashlib
+
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if "=" in line and line.strip().startswith("dense_decode_"):
+                key, val = (x.strip() for x in line.split("=", 1))
+                kv[key] = val
+        h = hashlib.sha256()
+        for f in DENSE_SOURCES:
+            with open(os.path.join(ROOT, "sparse_kv_amd", "csrc", f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != kv.get("dense_decode_source_sha256"):
+            return None
+        return int(kv["dense_decode_traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -41,11 +65,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--splits", type=int, default=16, help="splits per (batch row, KV head), dense stage")
-    ap.add_argument("--sparse-splits", type=int, default=12, help="splits per unit, sparse stage")
+    ap.add_argument("--sparse-splits", type=int, default=4, help="splits per unit, sparse stage")
     ap.add_argument("--window-splits", type=int, default=4, help="splits per unit, sink+window stage")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", default="dense,sparse,art,window")
+    ap.add_argument("--workload", default="decode128k", choices=["decode128k", "art64k", "hybrid256k"],
+                    help="decode128k (default): the 128K batch-8 step above; art64k: ART on the 64K batch-32 "
+                         "recency workload vs dense; hybrid256k: 36-layer routed stack at 256K vs all-full")
     return ap.parse_args()
 
 
@@ -55,6 +82,11 @@ def main():
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the decode path is single-device; see DESIGN.md for how it would shard).", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "art64k":
+        return bench_art64k(args)
+    if args.workload == "hybrid256k":
+        return bench_hybrid256k(args)
 
     import numpy as np
     import torch
@@ -235,12 +267,150 @@ def main():
         ach = kb / (paths["dense"]["kernel_ms"] * 1e-3) / 1e9
         res["roofline"] = {"kernel": "decode_kernel (split-KV dense)", "bound": "hbm", "achieved": round(ach, 1),
                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                           "traffic": None, "bytes_per_launch": kb,
+                           "traffic": measured_dense_traffic(), "bytes_per_launch": kb,
                            "avg_launch_ms": round(paths["dense"]["kernel_ms"], 5)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, topk, n_sink, n_recent, win_recent,
                                            tau, phi, patience, probe, total_bytes / units)
     print(json.dumps(res), flush=True)
+
+
+def _timer():
+    import torch
+
+    class T:
+        def __init__(self):
+            self.ev = []
+
+        def __enter__(self):
+            self.a = torch.cuda.Event(enable_timing=True)
+            self.b = torch.cuda.Event(enable_timing=True)
+            self.a.record()
+            return self
+
+        def __exit__(self, *exc):
+            self.b.record()
+            self.ev.append((self.a, self.b))
+
+        def avg_ms(self):
+            torch.cuda.synchronize()
+            return sum(a.elapsed_time(b) for a, b in self.ev) / len(self.ev)
+
+    return T()
+
+
+def _line(args, metric, value, unit, ms, config, **extra):
+    res = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config}
+    res.update(extra)
+    print(json.dumps(res), flush=True)
+
+
+def bench_art64k(args):
+    """ART on the 64K-context batch-32 recency workload, dense on the same inputs."""
+    import numpy as np
+    import torch
+
+    import sparse_kv_amd as skv
+    import synth
+
+    W = synth.WORKLOADS[4]
+    B, Hq, Hkv, d, L = W["B"], W["Hq"], W["Hkv"], W["d"], W["L"]
+    dev = torch.device("cuda", 0)
+    inp = synth.make_inputs(4, B, Hq, Hkv, d, L, kind="recency")
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    del inp
+    out, stop, fetched = skv.attn_decode_art(q, k, v, None, tau=W["tau"], phi=W["phi"], patience=W["patience"],
+                                             probe_dim=W["probe_dim"])
+    m, l, o = skv.attn_decode_dense(q, k, v, None, num_splits=16)
+    od = skv.attn_merge_states(m, l, o)
+    ta, td, t0, toff = _timer(), _timer(), _timer(), _timer()
+    for i in range(args.warmup + args.steps):
+        rec = i >= args.warmup
+        with (ta if rec else _timer()):
+            skv.attn_decode_art(q, k, v, None, tau=W["tau"], phi=W["phi"], patience=W["patience"],
+                                probe_dim=W["probe_dim"], out=out, stop_pos=stop, blocks_fetched=fetched)
+        with (td if rec else _timer()):
+            skv.attn_decode_dense(q, k, v, None, num_splits=16, m=m, l=l, o=o)
+            skv.attn_merge_states(m, l, o, out=od)
+    for i in range(3):  # detector overhead: no early exit (tau = phi = 0) vs detector off
+        with t0:
+            skv.attn_decode_art(q, k, v, None, tau=0.0, phi=0.0, patience=W["patience"], probe_dim=W["probe_dim"],
+                                out=out, stop_pos=stop, blocks_fetched=fetched)
+        with toff:
+            skv.attn_decode_art(q, k, v, None, tau=0.0, phi=0.0, patience=W["patience"], probe_dim=0,
+                                out=out, stop_pos=stop, blocks_fetched=fetched)
+    skv.attn_decode_art(q, k, v, None, tau=W["tau"], phi=W["phi"], patience=W["patience"], probe_dim=W["probe_dim"],
+                        out=out, stop_pos=stop, blocks_fetched=fetched)
+    ms_a, ms_d = ta.avg_ms(), td.avg_ms()
+    stp = stop.cpu().numpy().reshape(B, Hkv, Hq // Hkv)
+    need = stp.max(axis=2) + 1
+    kv_block = 64 * d * 4
+    by = float(need.sum()) * kv_block + B * Hq * d * 6
+    by_d = B * Hkv * (L // 64) * kv_block + B * Hq * d * 6
+    _line(args, "ART decode attention effective HBM GB/s (needed blocks / time), 64K ctx, batch 32",
+          by / (ms_a * 1e-3) / 1e9, "GB/s", ms_a,
+          {"workload": "ART decode step, 64K context, batch 32, 32 q / 8 kv heads, d 128, bf16 KV, recency-"
+                       "concentrated keys; tau 1e-3, phi 1e-4, patience 2, probe 8",
+           "batch": B, "context": L, "parallelism": "single-gpu"},
+          tokens_per_s=round(B / (ms_a * 1e-3), 1), dense_ms=round(ms_d, 4),
+          dense_gbs=round(by_d / (ms_d * 1e-3) / 1e9, 1), speedup_vs_dense=round(ms_d / ms_a, 3),
+          mean_stop=round(float(stp.mean()), 3), blocks_needed_per_unit=round(float(need.mean()), 3),
+          blocks_fetched_per_unit=round(float(fetched.float().mean()), 3),
+          detector_overhead_pct=round(100 * (t0.avg_ms() / toff.avg_ms() - 1), 3))
+
+
+def bench_hybrid256k(args):
+    """One decode step of the 36-layer routed stack at 256K context, batch 1."""
+    import numpy as np
+    import torch
+
+    import sparse_kv_amd as skv
+    import synth
+
+    W = synth.WORKLOADS[5]
+    B, Hq, Hkv, d, L = W["B"], W["Hq"], W["Hkv"], W["d"], W["L"]
+    nb = L // 64
+    dev = torch.device("cuda", 0)
+    mask = synth.route_mask(W["n_layers"], W["n_full"])
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    qs, ks, vs = [], [], []
+    t0 = time.perf_counter()
+    for i in range(W["n_layers"]):
+        inp = synth.make_inputs(5, B, Hq, Hkv, d, L, kind="needles", layer=i)
+        qs.append(up(inp.q))
+        ks.append(up(inp.k))
+        vs.append(up(inp.v))
+        del inp
+    print(f"[bench] generated 36 layers in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+    sa_idx, sa_n = skv.attn_select_topk(None, None, k=0, n_sink_blocks=W["n_sink"], n_recent_blocks=W["n_recent"],
+                                        shape=(B, Hkv, nb), device=dev)
+    kw = dict(n_shards=W["n_shards"], splits_per_shard=32, sa_block_idx=sa_idx, sa_n_sel=sa_n, sa_splits=8)
+    ws = torch.empty(skv.attn_routed_workspace_bytes(qs[0], ks[0], W["n_shards"], 32, 8), dtype=torch.uint8,
+                     device=dev)
+    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in qs]
+    th, tf = _timer(), _timer()
+    full = np.ones_like(mask)
+    for i in range(args.warmup + args.steps):
+        rec = i >= args.warmup
+        with (th if rec else _timer()):
+            skv.attn_decode_routed(qs, ks, vs, mask, None, workspace=ws, outs=outs, **kw)
+        with (tf if rec else _timer()):
+            skv.attn_decode_routed(qs, ks, vs, full, None, workspace=ws, outs=outs, **kw)
+    ms_h, ms_f = th.avg_ms(), tf.avg_ms()
+    kv_block = 64 * d * 4
+    n_sa = float(sa_n.sum().item())
+    by = sum((B * Hkv * nb if m_ else n_sa) * kv_block for m_ in mask) + len(mask) * B * Hq * d * 6
+    by_f = len(mask) * B * Hkv * nb * kv_block + len(mask) * B * Hq * d * 6
+    _line(args, "routed hybrid decode HBM GB/s, 36 layers, 256K ctx, batch 1", by / (ms_h * 1e-3) / 1e9, "GB/s",
+          ms_h, {"workload": "one decode step through a 36-layer routed stack (18 full / 18 sink+window), "
+                             "256K context, batch 1, 32 q / 8 kv heads, d 128, bf16 KV; full layers as 8 "
+                             "context shards x 32 splits", "batch": B, "context": L, "parallelism": "single-gpu"},
+          tokens_per_s=round(B / (ms_h * 1e-3), 2), all_full_ms=round(ms_f, 4),
+          all_full_gbs=round(by_f / (ms_f * 1e-3) / 1e9, 1), speedup_vs_all_full=round(ms_f / ms_h, 3),
+          byte_ratio=round(by_f / by, 3))
 
 
 def cpu_baseline(inp, budget_s, topk, n_sink, n_recent, win_recent, tau, phi, patience, probe, bytes_per_unit):

@@ -107,6 +107,26 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+class _on_device:
+    """Make `dev` current for the duration of a call (cheap when it already is)."""
+
+    __slots__ = ("dev", "prev")
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.prev = None
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if cur != self.dev.index:
+            self.prev = cur
+            torch.cuda.set_device(self.dev)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+
+
 def _dtype_code(t):
     if t.dtype == torch.bfloat16:
         return ATTN_BF16
@@ -177,7 +197,7 @@ def attn_decode_dense(q, k, v, seq_lens=None, num_splits=16, block_begin=0, bloc
     m = _out(m, rows, torch.float32, dev, "m")
     l = _out(l, rows, torch.float32, dev, "l")
     o = _out(o, rows + (dims.head_dim,), torch.float32, dev, "o")
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib().attn_decode_dense(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(seq),
                                     int(block_begin), int(block_end), int(num_splits),
                                     _ptr(m), _ptr(l), _ptr(o), _stream(dev))
@@ -207,7 +227,7 @@ def attn_merge_states(m, l, o, out=None, m_out=None, l_out=None):
     if want_state:
         _need(m_out, "m_out", dev, torch.float32, lead)
         _need(l_out, "l_out", dev, torch.float32, lead)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib().attn_merge_states(rows, S, d, _ptr(m), _ptr(l), _ptr(o), _ptr(out),
                                     _ptr(m_out) if want_state else None,
                                     _ptr(l_out) if want_state else None, _stream(dev))
@@ -225,7 +245,7 @@ def attn_build_centroids(k, seq_lens=None, out=None, num_q_heads=None):
     dims = AttnDims(B, num_q_heads or Hkv, Hkv, d, BLOCK, Lmax // BLOCK, _dtype_code(k), 1.0)
     seq = _seq(seq_lens, B, dev)
     out = _out(out, (B, Hkv, Lmax // BLOCK, d), torch.float32, dev, "out")
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib().attn_build_centroids(ctypes.byref(dims), _ptr(k), _ptr(seq), _ptr(out), _stream(dev))
     _check(st, "attn_build_centroids")
     return out
@@ -244,7 +264,7 @@ def attn_score_centroids(q, centroids, seq_lens=None, scale=None, out=None):
     dims = AttnDims(B, Hq, Hkv, d, BLOCK, NBmax, _dtype_code(q), s)
     seq = _seq(seq_lens, B, dev)
     out = _out(out, (B, Hkv, NBmax), torch.float32, dev, "out")
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib().attn_score_centroids(ctypes.byref(dims), _ptr(q), _ptr(centroids), _ptr(seq),
                                        _ptr(out), _stream(dev))
     _check(st, "attn_score_centroids")
@@ -272,7 +292,7 @@ def attn_select_topk(scores, seq_lens=None, k=0, n_sink_blocks=1, n_recent_block
     seq = _seq(seq_lens, B, dev)
     block_idx = _out(block_idx, (B, Hkv, max_sel), torch.int32, dev, "block_idx")
     n_sel = _out(n_sel, (B, Hkv), torch.int32, dev, "n_sel")
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib().attn_select_topk(ctypes.byref(dims), _ptr(scores), _ptr(seq), int(k), int(n_sink_blocks),
                                    int(n_recent_blocks), int(max_sel), _ptr(block_idx), _ptr(n_sel),
                                    _stream(dev))
@@ -297,7 +317,7 @@ def attn_decode_sparse(q, k, v, block_idx, n_sel, seq_lens=None, num_splits=4, s
     m = _out(m, rows, torch.float32, dev, "m")
     l = _out(l, rows, torch.float32, dev, "l")
     o = _out(o, rows + (dims.head_dim,), torch.float32, dev, "o")
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib().attn_decode_sparse(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(seq),
                                      _ptr(block_idx), _ptr(n_sel), int(block_idx.shape[2]),
                                      int(num_splits), _ptr(m), _ptr(l), _ptr(o), _stream(dev))
@@ -319,7 +339,7 @@ def attn_decode_art(q, k, v, seq_lens=None, order=None, tau=1e-3, phi=1e-4, pati
     out = _out(out, (dims.batch, dims.num_q_heads, dims.head_dim), torch.float32, dev, "out")
     stop_pos = _out(stop_pos, (dims.batch, dims.num_q_heads), torch.int32, dev, "stop_pos")
     blocks_fetched = _out(blocks_fetched, (dims.batch, dims.num_kv_heads), torch.int32, dev, "blocks_fetched")
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib().attn_decode_art(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(seq), _ptr(order),
                                   float(tau), float(phi), int(patience), int(probe_dim), _ptr(out),
                                   _ptr(stop_pos), _ptr(blocks_fetched), _stream(dev))
@@ -370,7 +390,7 @@ def attn_decode_routed(qs, ks, vs, route_mask, seq_lens=None, n_shards=8, splits
     va = arr(*[t.data_ptr() for t in vs])
     oa = arr(*[t.data_ptr() for t in outs])
     max_sel = int(sa_block_idx.shape[-1]) if sa_block_idx is not None else 0
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib().attn_decode_routed(ctypes.byref(dims), n, ctypes.cast(mask, _P), ctypes.cast(qa, _P),
                                      ctypes.cast(ka, _P), ctypes.cast(va, _P), _ptr(seq), int(n_shards),
                                      int(splits_per_shard), _ptr(sa_block_idx), _ptr(sa_n_sel), max_sel,

@@ -8,11 +8,11 @@
 // p consecutive blocks (§2.3).
 //
 // One workgroup = one (b, kv head), split by role:
-//   * 7 producer waves stream blocks: producer i takes visit positions
-//     i, i+7, i+14, ...; for each it loads the block (16-byte buffer loads),
+//   * NP producer waves (7, or 15 when the grid has fewer units than CUs)
+//     stream blocks: producer i takes visit positions i, i+NP, i+2NP, ...; for each it loads the block (16-byte buffer loads),
 //     forms the G x 64 logits on MFMA, the block-local softmax, and P.V in
 //     fp32, and publishes the block's state (m, l, unnormalised P.V of all
-//     channels) into an 8-slot ring in LDS.
+//     channels) into an R-slot ring in LDS (R = NP + 1).
 //   * 1 folder wave folds the published states strictly in visit order into
 //     the running state -- the exact sequence of a one-block-at-a-time
 //     streaming kernel -- and after every fold evaluates the stop rule per
@@ -20,9 +20,9 @@
 //     that stops freezes its state; when every head of the group has
 //     stopped (or the blocks run out) the folder writes the outputs.
 // Ring protocol (acquire/release on LDS words): a producer may start
-// position t only once position t-8 has been folded, so read-ahead past the
-// final stop is at most 8 blocks (counted in blocks_fetched); the folder
-// waits for slot t%8 to hold position t.  The folder is never blocked by a
+// position t only once position t-R has been folded, so read-ahead past the
+// final stop is at most R blocks (counted in blocks_fetched); the folder
+// waits for slot t%R to hold position t.  The folder is never blocked by a
 // producer that is itself blocked: the owner of the next position to fold
 // always has its slot free.  Producers leave when the folder signals done.
 #include "device_common.hpp"
@@ -31,8 +31,6 @@
 namespace skv {
 namespace {
 
-constexpr int kNP = 7;  // producer waves
-constexpr int kR = 8;   // ring slots = read-ahead bound
 
 __device__ __forceinline__ int ld_acq(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -41,26 +39,29 @@ __device__ __forceinline__ void st_rel(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-template <typename T, int D, int GR>
+// NP producer waves, R ring slots (R also bounds the read-ahead).
+template <typename T, int D, int GR, int NP, int R>
 struct ArtShared {
   static constexpr int GP = 4 * GR;
-  float p_lds[kNP][64 * GP];
-  float slot_acc[kR][GP][D];
-  float slot_m[kR][GP];
-  float slot_l[kR][GP];
-  int slot_pos[kR];
+  static constexpr int kNP = NP, kR = R;
+  float p_lds[NP][64 * GP];
+  float slot_acc[R][GP][D];
+  float slot_m[R][GP];
+  float slot_l[R][GP];
+  int slot_pos[R];
   int folded;
   int done;
   int fetched;
 };
 
-template <typename T, int D, int GR>
-__device__ void art_producer(const ArtArgs& p, ArtShared<T, D, GR>& sh, int pi, int unit, int b, int g, int G,
+template <typename T, int D, int GR, typename SH>
+__device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, int g, int G,
                              int L, int nb) {
   using Gm = Geo<T, D>;
   constexpr int GP = 4 * GR;
   constexpr int E = Gm::E, CPR = Gm::CPR, TPI = Gm::TPI, KA = Gm::KA, ROWB = Gm::ROWB;
   constexpr bool BF = sizeof(T) == 2;
+  constexpr int kNP = SH::kNP, kR = SH::kR;
   const int lane = threadIdx.x & 63;
   const int NBmax = p.NBmax;
 
@@ -203,9 +204,10 @@ __device__ void art_producer(const ArtArgs& p, ArtShared<T, D, GR>& sh, int pi, 
   }
 }
 
-template <typename T, int D, int GR>
-__device__ void art_folder(const ArtArgs& p, ArtShared<T, D, GR>& sh, int b, int g, int G, int nb) {
+template <typename T, int D, int GR, typename SH>
+__device__ void art_folder(const ArtArgs& p, SH& sh, int b, int g, int G, int nb) {
   constexpr int FE = D / 16;  // channels per folder lane: lane = 16 * (q % 4) + c
+  constexpr int kR = SH::kR;
   const int lane = threadIdx.x & 63;
   const int q4 = lane >> 4, c = lane & 15;
   const int P = p.probe_dim;
@@ -297,9 +299,10 @@ __device__ void art_folder(const ArtArgs& p, ArtShared<T, D, GR>& sh, int b, int
   }
 }
 
-template <typename T, int D, int GR>
-__global__ __launch_bounds__((kNP + 1) * 64) void art_kernel(ArtArgs p) {
-  __shared__ ArtShared<T, D, GR> sh;
+template <typename T, int D, int GR, int NP, int R>
+__global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
+  using SH = ArtShared<T, D, GR, NP, R>;
+  __shared__ SH sh;
   const int unit = blockIdx.x;
   const int b = unit / p.Hkv, g = unit % p.Hkv;
   const int w = threadIdx.x >> 6;
@@ -307,29 +310,44 @@ __global__ __launch_bounds__((kNP + 1) * 64) void art_kernel(ArtArgs p) {
   const int NBmax = p.NBmax;
   const int L = clampi(p.seq_lens ? p.seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
   const int nb = (L + kBlock - 1) / kBlock;
-  if (threadIdx.x < kR) sh.slot_pos[threadIdx.x] = -1;
+  if (threadIdx.x < R) sh.slot_pos[threadIdx.x] = -1;
   if (threadIdx.x == 0) {
     sh.folded = 0;
     sh.done = 0;
     sh.fetched = 0;
   }
   __syncthreads();
-  if (w == 0)
-    art_folder<T, D, GR>(p, sh, b, g, G, nb);
+  if (w == 0) {
+    // the folder is the serial chain of the kernel: let the SIMD arbiter
+    // prefer it over the producer waves that share its SIMD
+    __builtin_amdgcn_s_setprio(3);
+    art_folder<T, D, GR, SH>(p, sh, b, g, G, nb);
+  }
   else
-    art_producer<T, D, GR>(p, sh, w - 1, unit, b, g, G, L, nb);
+    art_producer<T, D, GR, SH>(p, sh, w - 1, unit, b, g, G, L, nb);
   __syncthreads();
   if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[unit] = sh.fetched;
 }
 
+// With at least one (b, kv head) unit per CU the chip is bandwidth-bound and
+// the 8-block read-ahead keeps over-fetch small; with fewer units each
+// workgroup must pull more bandwidth by itself, so it gets 15 producers and a
+// 16-block window.
 template <typename T, int D>
 hipError_t launch_art_t(const ArtArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
-  const dim3 grid(a.B * a.Hkv);
-  if (G <= 4)
-    art_kernel<T, D, 1><<<grid, (kNP + 1) * 64, 0, st>>>(a);
+  const int units = a.B * a.Hkv;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const dim3 grid(units);
+  if (G > 4)
+    art_kernel<T, D, 2, 7, 8><<<grid, 8 * 64, 0, st>>>(a);
+  else if (units >= cus)
+    art_kernel<T, D, 1, 7, 8><<<grid, 8 * 64, 0, st>>>(a);
   else
-    art_kernel<T, D, 2><<<grid, (kNP + 1) * 64, 0, st>>>(a);
+    art_kernel<T, D, 1, 15, 16><<<grid, 16 * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ def check_fetched(fetched, stop, inp):
         nb = -(-int(inp.seq_lens[b]) // 64)
         for g in range(Hkv):
             need = int(stop[b, g * G:(g + 1) * G].max()) + 1
-            assert need <= fetched[b, g] <= min(nb, need + 8), (b, g, need, fetched[b, g])
+            assert need <= fetched[b, g] <= min(nb, need + 16), (b, g, need, fetched[b, g])
 
 
 @pytest.mark.parametrize("label,B,Hq,Hkv,d,L,seq,dt", [

@@ -1,0 +1,153 @@
+"""GPU parity at the workloads' full sizes, in the launch configurations the
+benchmark uses; the oracle checks sampled (batch row, KV head) units."""
+
+import math
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.art import art_margin_ok
+from oracle.selection import forced_blocks, selection_gap
+from tests.gpu_util import TOL, assert_close, log
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = [(0, 0), (3, 5), (7, 7)]  # (batch row, KV head) units checked against the oracle
+
+
+def up(a, dtype="bf16"):
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def unit_f64(inp, b, g):
+    G = inp.q.shape[1] // inp.k.shape[1]
+    q = inp.upcast(inp.q[b:b + 1, g * G:(g + 1) * G])
+    k = inp.upcast(inp.k[b:b + 1, g:g + 1])
+    v = inp.upcast(inp.v[b:b + 1, g:g + 1])
+    return q, k, v, inp.seq_lens[b:b + 1]
+
+
+def test_llama_dense_32k_batch8_16_splits():
+    W = synth.WORKLOADS[2]
+    t = time.time()
+    inp = synth.make_inputs(2, W["B"], W["Hq"], W["Hkv"], W["d"], W["L"], kind=W["kind"])
+    log(f"[full] dense 32K batch 8: inputs in {time.time() - t:.1f}s")
+    import sparse_kv_amd as skv
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    out = skv.attn_merge_states(*skv.attn_decode_dense(q, k, v, None, num_splits=W["splits"]))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    G = W["Hq"] // W["Hkv"]
+    for b, g in SAMPLE:
+        qf, kf, vf, seq = unit_f64(inp, b, g)
+        ref = oracle.decode_dense(qf, kf, vf, seq, inp.scale)
+        assert_close(out[b, g * G:(g + 1) * G], ref[0], TOL, f"unit ({b},{g})")
+
+
+def test_sparse_128k_batch8_selection_and_dense():
+    W = synth.WORKLOADS[3]
+    B, Hq, Hkv, d, L = W["B"], W["Hq"], W["Hkv"], W["d"], W["L"]
+    k_top, ns, nr = W["topk"], W["n_sink"], W["n_recent"]
+    t = time.time()
+    inp = synth.make_inputs(3, B, Hq, Hkv, d, L, kind="mixture")
+    log(f"[full] 128K batch 8: inputs in {time.time() - t:.1f}s")
+    import sparse_kv_amd as skv
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    dense = skv.attn_merge_states(*skv.attn_decode_dense(q, k, v, None, num_splits=16))
+    C = skv.attn_build_centroids(k)
+    sc = skv.attn_score_centroids(q, C)
+    idx, n = skv.attn_select_topk(sc, None, k=k_top, n_sink_blocks=ns, n_recent_blocks=nr)
+    sp = skv.attn_merge_states(*skv.attn_decode_sparse(q, k, v, idx, n, None, num_splits=12))
+    torch.cuda.synchronize()
+    dense, sp, idx, n = dense.cpu().numpy(), sp.cpu().numpy(), idx.cpu().numpy(), n.cpu().numpy()
+    assert (n == ns + nr + k_top).all()
+    G = Hq // Hkv
+    checked = 0
+    for b, g in SAMPLE:
+        qf, kf, vf, seq = unit_f64(inp, b, g)
+        assert_close(dense[b, g * G:(g + 1) * G], oracle.decode_dense(qf, kf, vf, seq, inp.scale)[0], TOL,
+                     f"dense unit ({b},{g})")
+        sig = oracle.centroid_scores(qf, oracle.block_centroids(kf, seq), seq, inp.scale)
+        gap = selection_gap(sig[0, 0], L // 64, k_top, ns, nr)
+        lists = oracle.select_all(sig, seq, k_top, ns, nr)
+        log(f"  unit ({b},{g}): top-k boundary gap {gap:.2e}")
+        if gap > 1e-4:
+            assert idx[b, g, :n[b, g]].tolist() == lists[0][0], f"selected blocks of unit ({b},{g})"
+            checked += 1
+        got = [[idx[b, g, :n[b, g]].tolist()]]
+        ref = oracle.decode_blocks(qf, kf, vf, seq, inp.scale, got)
+        assert_close(sp[b, g * G:(g + 1) * G], ref[0], TOL, f"sparse unit ({b},{g})")
+    assert checked >= 2, "too few sampled units with a clear top-k margin"
+
+
+def test_art_64k_batch32_stop_positions():
+    W = synth.WORKLOADS[4]
+    B, Hq, Hkv, d, L = W["B"], W["Hq"], W["Hkv"], W["d"], W["L"]
+    t = time.time()
+    inp = synth.make_inputs(4, B, Hq, Hkv, d, L, kind="recency")
+    log(f"[full] ART 64K batch 32: inputs in {time.time() - t:.1f}s")
+    import sparse_kv_amd as skv
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    out, stop, fetched = skv.attn_decode_art(q, k, v, None, tau=W["tau"], phi=W["phi"], patience=W["patience"],
+                                             probe_dim=W["probe_dim"])
+    torch.cuda.synchronize()
+    out, stop, fetched = out.cpu().numpy(), stop.cpu().numpy(), fetched.cpu().numpy()
+    G = Hq // Hkv
+    log(f"  mean stop {stop.mean():.2f}, mean blocks fetched {fetched.mean():.2f}")
+    for b, g in SAMPLE + [(31, 0), (16, 3)]:
+        qf, kf, vf, seq = unit_f64(inp, b, g)
+        ro, rs, tr = oracle.art_decode(qf, kf, vf, seq, inp.scale, W["tau"], W["phi"], W["patience"], W["probe_dim"])
+        assert all(art_margin_ok(x, W["tau"], W["phi"]) for x in tr.values()), f"unit ({b},{g}) lacks margins"
+        assert stop[b, g * G:(g + 1) * G].tolist() == rs[0].tolist(), f"stop positions of unit ({b},{g})"
+        assert_close(out[b, g * G:(g + 1) * G], ro[0], TOL, f"ART unit ({b},{g})")
+        need = int(rs.max()) + 1
+        assert need <= fetched[b, g] <= need + 8, (b, g, need, fetched[b, g])
+
+
+def test_routed_36_layer_stack_256k():
+    W = synth.WORKLOADS[5]
+    B, Hq, Hkv, d, L = W["B"], W["Hq"], W["Hkv"], W["d"], W["L"]
+    nb = L // 64
+    mask = synth.route_mask(W["n_layers"], W["n_full"])
+    import sparse_kv_amd as skv
+
+    keep = [[sorted(forced_blocks(nb, W["n_sink"], W["n_recent"]))] * Hkv]
+    t = time.time()
+    qs, ks, vs, host = [], [], [], {}
+    check = {int(np.flatnonzero(mask == 1)[0]), int(np.flatnonzero(mask == 0)[0])}
+    for i in range(W["n_layers"]):
+        inp = synth.make_inputs(5, B, Hq, Hkv, d, L, kind="needles", layer=i)
+        if i in check:
+            host[i] = (unit_f64(inp, 0, 2), unit_f64(inp, 0, 6))  # clean copies, before any poisoning
+        if not mask[i]:
+            synth.poison_blocks(inp, keep)  # a sink + window layer must never read these
+        qs.append(up(inp.q))
+        ks.append(up(inp.k))
+        vs.append(up(inp.v))
+        del inp
+    log(f"[full] 36-layer 256K stack: inputs in {time.time() - t:.1f}s")
+    sa_idx, sa_n = skv.attn_select_topk(None, None, k=0, n_sink_blocks=W["n_sink"], n_recent_blocks=W["n_recent"],
+                                        shape=(B, Hkv, nb), device="cuda")
+    outs = skv.attn_decode_routed(qs, ks, vs, mask, None, n_shards=W["n_shards"], splits_per_shard=32,
+                                  sa_block_idx=sa_idx, sa_n_sel=sa_n, sa_splits=8)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    for i in sorted(check):
+        for (qf, kf, vf, seq), g in zip(host[i], (2, 6)):
+            if mask[i]:
+                ref = oracle.decode_dense(qf, kf, vf, seq, 1 / math.sqrt(d))
+            else:
+                ref = oracle.decode_blocks(qf, kf, vf, seq, 1 / math.sqrt(d), [[keep[0][0]]])
+            assert_close(outs[i][0, g * G:(g + 1) * G].cpu().numpy(), ref[0], TOL,
+                         f"layer {i} ({'FA' if mask[i] else 'SA'}) kv head {g}")
+    for o in outs:
+        assert torch.isfinite(o).all()
