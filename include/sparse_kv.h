@@ -43,7 +43,8 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = -1, /* a NULL required pointer, a bad size or dim      */
-  ATTN_ERR_UNSUPPORTED = -2, /* valid but not built: d not in {64,128}, G > 8 */
+  ATTN_ERR_UNSUPPORTED = -2, /* valid but not built: d not in {64,128}, G > 8,
+                                a head's K slice above 2 GiB                  */
   ATTN_ERR_HIP = -3,         /* a launch or HIP runtime call failed             */
   ATTN_ERR_WORKSPACE = -4    /* the workspace given is too small                */
 } attn_status;
@@ -56,7 +57,8 @@ typedef struct {
   int32_t num_kv_heads; /* Hkv >= 1; G = Hq / Hkv must be <= 8             */
   int32_t head_dim;     /* d: 64 or 128                                     */
   int32_t block_size;   /* must be 64                                       */
-  int32_t max_blocks;   /* NB_max >= 1: K/V hold NB_max * 64 rows per head */
+  int32_t max_blocks;   /* NB_max >= 1: K/V hold NB_max * 64 rows per head;
+                           one head's K (or V) slice must fit in 2 GiB       */
   int32_t dtype;        /* attn_dtype                                       */
   float scale;          /* logit scale, normally 1 / sqrt(d)                */
 } attn_dims;

@@ -23,9 +23,10 @@ int check_dims(const attn_dims* d) {
   if (d->head_dim != 64 && d->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (d->block_size != 64) return ATTN_ERR_UNSUPPORTED;
   if (d->num_q_heads / d->num_kv_heads > 8) return ATTN_ERR_UNSUPPORTED;
-  // one (b, kv head) slice of K or V must be addressable with 32-bit offsets
+  // one (b, kv head) slice of K or V is addressed with 32-bit buffer offsets;
+  // offsets from 2 GiB up are reserved as "no block" (reads return zeros)
   const uint64_t row_bytes = (uint64_t)d->head_dim * (d->dtype == ATTN_BF16 ? 2 : 4);
-  if ((uint64_t)d->max_blocks * 64 * row_bytes >= (1ull << 32)) return ATTN_ERR_UNSUPPORTED;
+  if ((uint64_t)d->max_blocks * 64 * row_bytes > (1ull << 31)) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 

@@ -8,15 +8,17 @@
 // p consecutive blocks (§2.3).
 //
 // One workgroup = one (b, kv head), split by role:
-//   * NP producer waves (7, or 15 when the grid has fewer units than CUs)
-//     stream blocks: producer i takes visit positions i, i+NP, i+2NP, ...; for each it loads the block (16-byte buffer loads),
+//   * 7 producer waves stream blocks: producer i takes visit positions
+//     i, i+7, i+14, ... (loads software-pipelined across positions when the
+//     grid has fewer units than CUs); for each it loads the block (16-byte buffer loads),
 //     forms the G x 64 logits on MFMA, the block-local softmax, and P.V in
 //     fp32, and publishes the block's state (m, l, unnormalised P.V of all
-//     channels) into an R-slot ring in LDS (R = NP + 1).
+//     channels) into an R-slot ring in LDS (R = 8, or 16 when pipelined).
 //   * 1 folder wave folds the published states strictly in visit order into
 //     the running state -- the exact sequence of a one-block-at-a-time
 //     streaming kernel -- and after every fold evaluates the stop rule per
-//     query head on the probe channels (one 16-lane row per head).  A head
+//     query head on the probe channels (one decision lane per head, so the
+//     serial chain has no cross-lane reductions).  A head
 //     that stops freezes its state; when every head of the group has
 //     stopped (or the blocks run out) the folder writes the outputs.
 // Ring protocol (acquire/release on LDS words): a producer may start
@@ -39,11 +41,13 @@ __device__ __forceinline__ void st_rel(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// NP producer waves, R ring slots (R also bounds the read-ahead).
-template <typename T, int D, int GR, int NP, int R>
+// NP producer waves, R ring slots (R also bounds the read-ahead), PF: producers
+// software-pipeline their loads across positions.
+template <typename T, int D, int GR, int NP, int R, bool PF>
 struct ArtShared {
   static constexpr int GP = 4 * GR;
   static constexpr int kNP = NP, kR = R;
+  static constexpr bool kPF = PF;
   float p_lds[NP][64 * GP];
   float slot_acc[R][GP][D];
   float slot_m[R][GP];
@@ -54,9 +58,13 @@ struct ArtShared {
   int fetched;
 };
 
+// Producer wave pi: visit positions pi, pi + NP, ...  With SH::kPF the loads
+// are software-pipelined as in the split-KV kernel: the next position's K is
+// requested right after this block's logits and its V right after this
+// block's P.V (when the read-ahead window already allows it), so HBM latency
+// hides behind this block's arithmetic with no extra registers.
 template <typename T, int D, int GR, typename SH>
-__device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, int g, int G,
-                             int L, int nb) {
+__device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, int g, int G, int L, int nb) {
   using Gm = Geo<T, D>;
   constexpr int GP = 4 * GR;
   constexpr int E = Gm::E, CPR = Gm::CPR, TPI = Gm::TPI, KA = Gm::KA, ROWB = Gm::ROWB;
@@ -84,30 +92,47 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
   const int phase = lane / CPR;
   float* pl = sh.p_lds[pi];
 
-  for (int t = pi; t < nb; t += kNP) {
-    // bounded read-ahead: position t may start once t - kR has been folded
-    bool go = false;
+  auto block_of = [&](int t) {
+    return p.order ? clampi(p.order[(size_t)unit * NBmax + t], 0, nb - 1) : (t == 0 ? 0 : nb - t);
+  };
+  // read-ahead window: position t may start once t - kR has been folded
+  auto window_open = [&](int t) { return ld_acq(&sh.folded) > t - kR; };
+  auto window_wait = [&](int t) {
     while (true) {
-      if (ld_acq(&sh.done)) break;
-      if (ld_acq(&sh.folded) > t - kR) {
-        go = true;
-        break;
-      }
+      if (ld_acq(&sh.done)) return false;
+      if (window_open(t)) return true;
       __builtin_amdgcn_s_sleep(1);
     }
-    if (!go) return;
-    if (lane == 0) atomicAdd(&sh.fetched, 1);
-    const int j = p.order ? clampi(p.order[(size_t)unit * NBmax + t], 0, nb - 1) : (t == 0 ? 0 : nb - t);
-    const uint32_t soff = (uint32_t)j * kBlock * ROWB;
-    u32x4 kr[4][KA];
+  };
+  u32x4 kr[4][KA], vr[CPR];
+  // soff = byte offset of a block, or kNoBlock: past the buffers' range limit
+  // (slices are at most 2 GiB), so the loads return zeros and touch no memory
+  constexpr uint32_t kNoBlock = 0x80000000u;
+  auto load_k = [&](uint32_t soff) {
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
       for (int a = 0; a < KA; ++a) kr[t4][a] = load16(krs, soff + kvo + t4 * 16 * ROWB + a * 64, 0);
-    u32x4 vr[CPR];
+  };
+  auto load_v = [&](uint32_t soff) {
 #pragma unroll
     for (int i = 0; i < CPR; ++i) vr[i] = load16_nt(vrs, soff + vvo + i * TPI * ROWB, 0);
+  };
+  auto block_off = [&](int j) {
+    if (lane == 0) atomicAdd(&sh.fetched, 1);
+    return (uint32_t)j * kBlock * ROWB;
+  };
 
+  int t = pi;
+  if (t >= nb || !window_wait(t)) return;
+  int j = block_of(t);
+  {
+    const uint32_t so = block_off(j);
+    load_k(so);
+    load_v(so);
+  }
+  while (true) {
+    const int tn = t + kNP;
     f32x4 sc[4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
@@ -123,6 +148,19 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
         }
       }
       sc[t4] = c;
+    }
+    bool pf = false;
+    int jn = 0;
+    uint32_t son = kNoBlock;
+    if constexpr (SH::kPF) {
+      // unconditional loads keep one register lifetime; a closed window
+      // aims them past the range limit
+      pf = tn < nb && !ld_acq(&sh.done) && window_open(tn);
+      if (pf) {
+        jn = block_of(tn);
+        son = block_off(jn);
+      }
+      load_k(son);
     }
     const int nvalid = min(kBlock, L - j * kBlock);
     float mb[GR], lb[GR];
@@ -179,13 +217,12 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
 #pragma unroll
         for (int e = 0; e < E; ++e) ab[q][e] = fmaf(pq[q], vf[e], ab[q][e]);
     }
+    if constexpr (SH::kPF) load_v(son);
     // sum the token phases, publish the block state, then its position
 #pragma unroll
     for (int q = 0; q < GP; ++q)
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-#pragma unroll
-        for (int off = CPR; off < 64; off <<= 1) ab[q][e] += __shfl_xor(ab[q][e], off);
+      for (int e = 0; e < E; ++e) ab[q][e] = phase_sum<CPR>(ab[q][e]);
     const int s = t % kR;
     if (lane < CPR) {
 #pragma unroll
@@ -201,107 +238,148 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
       }
     }
     if (lane == 0) st_rel(&sh.slot_pos[s], t);
+
+    if (tn >= nb) return;
+    if (!pf) {
+      if (!window_wait(tn)) return;
+      jn = block_of(tn);
+      const uint32_t so = block_off(jn);
+      load_k(so);
+      load_v(so);
+    }
+    t = tn;
+    j = jn;
   }
 }
 
+// The folder wave.  Lane q < G is the decision lane of query head q: it keeps
+// that head's running max and denominator and the probe channels of its
+// running output, and evaluates the stop rule with no cross-lane traffic.
+// Every lane (row q % 4, channels c * FE ..) also folds its slice of the full
+// running output with the decision lanes' rescale factors, read back with
+// readlane; a head stops contributing after its stop position.
 template <typename T, int D, int GR, typename SH>
 __device__ void art_folder(const ArtArgs& p, SH& sh, int b, int g, int G, int nb) {
-  constexpr int FE = D / 16;  // channels per folder lane: lane = 16 * (q % 4) + c
+  constexpr int FE = D / 16;  // output channels per lane
+  constexpr int PW = 16;      // probe channels a decision lane can hold (probe_dim <= 16)
   constexpr int kR = SH::kR;
   const int lane = threadIdx.x & 63;
   const int q4 = lane >> 4, c = lane & 15;
   const int P = p.probe_dim;
-  float M[GR], Ls[GR], A[GR][FE], xp[GR][FE], n0[GR];  // xp: previous unit probe
-  int cnt[GR], stopT[GR];
+  const bool dec = lane < G;
+  const int dq = dec ? lane : 0;
+
+  float dM = -INFINITY, dL = 0.f, dn0 = 0.f;
+  float dA[PW], du[PW];
 #pragma unroll
-  for (int r = 0; r < GR; ++r) {
-    M[r] = -INFINITY;
-    Ls[r] = 0.f;
-    n0[r] = 0.f;
-    cnt[r] = 0;
-    stopT[r] = -1;
-#pragma unroll
-    for (int e = 0; e < FE; ++e) {
-      A[r][e] = 0.f;
-      xp[r][e] = 0.f;
-    }
+  for (int k = 0; k < PW; ++k) {
+    dA[k] = 0.f;
+    du[k] = 0.f;
   }
+  int dcnt = 0, dstop = -1;
+  float A[GR][FE];
+#pragma unroll
+  for (int r = 0; r < GR; ++r)
+#pragma unroll
+    for (int e = 0; e < FE; ++e) A[r][e] = 0.f;
+
   for (int t = 0; t < nb; ++t) {
     const int s = t % kR;
     while (ld_acq(&sh.slot_pos[s]) != t) __builtin_amdgcn_s_sleep(1);
-    bool live = false;
+    // the block's slice of the full output for this lane
+    float a[GR][FE];
+#pragma unroll
+    for (int r = 0; r < GR; ++r)
+#pragma unroll
+      for (int e = 0; e < FE; ++e) a[r][e] = sh.slot_acc[s][4 * r + q4][c * FE + e];
+
+    // decision lanes: fold m, l and the probe channels, then the stop rule
+    float al = 1.f, be = 0.f;
+    int inc = 0;
+    if (dec && dstop < 0) {
+      inc = 1;
+      const float mb = sh.slot_m[s][dq], lb = sh.slot_l[s][dq];
+      const float Mn = fmaxf(dM, mb);
+      al = fast_exp2(dM - Mn);
+      be = fast_exp2(mb - Mn);
+      dL = al * dL + be * lb;
+      dM = Mn;
+      if (P > 0) {
+        const float rl = fast_rcp(dL);
+        float x[PW];
+        float n2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < PW; ++k) {
+          const float ak = k < P ? sh.slot_acc[s][dq][k] : 0.f;
+          dA[k] = al * dA[k] + be * ak;
+          x[k] = dA[k] * rl;
+          n2 = fmaf(x[k], x[k], n2);
+        }
+        const float i1 = n2 > 0.f ? fast_rsq(n2) : 0.f;
+        const float n1 = n2 * i1;
+        float u2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < PW; ++k) {
+          const float uk = x[k] * i1;
+          const float d = uk - du[k];
+          u2 = fmaf(d, d, u2);
+          du[k] = uk;
+        }
+        if (t >= 1) {
+          const float ds = fabsf(n1 - dn0);
+          // 1 - cos as half the squared distance of the unit vectors
+          const float dd = (n1 > 0.f && dn0 > 0.f) ? 0.5f * u2 : INFINITY;
+          const bool stable = ds < p.tau && dd < p.phi;
+          dcnt = stable ? dcnt + 1 : 0;
+          if (dcnt >= p.patience) dstop = t;
+        }
+        dn0 = n1;
+      }
+    }
+    // every lane folds its slice of the full output with its head's factors
 #pragma unroll
     for (int r = 0; r < GR; ++r) {
-      const int q = 4 * r + q4;
-      if (q < G && stopT[r] < 0) {  // uniform over the 16-lane row
-        const float mq = sh.slot_m[s][q], lq = sh.slot_l[s][q];
-        const float Mn = fmaxf(M[r], mq);
-        const float al = fast_exp2(M[r] - Mn), be = fast_exp2(mq - Mn);
+      float alr = 1.f, ber = 0.f;
+      int incr = 0;
 #pragma unroll
-        for (int e = 0; e < FE; ++e) A[r][e] = al * A[r][e] + be * sh.slot_acc[s][q][c * FE + e];
-        Ls[r] = al * Ls[r] + be * lq;
-        M[r] = Mn;
-        if (P > 0) {
-          // probe x = A / L on the first P channels; unit vector u = x / |x|
-          const float rl = fast_rcp(Ls[r]);
-          float x[FE];
-          float n2 = 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const float aj = readlane(al, 4 * r + j), bj = readlane(be, 4 * r + j);
+        const int ij = __builtin_amdgcn_readlane(inc, 4 * r + j);
+        alr = q4 == j ? aj : alr;
+        ber = q4 == j ? bj : ber;
+        incr = q4 == j ? ij : incr;
+      }
+      if (incr) {
 #pragma unroll
-          for (int e = 0; e < FE; ++e) {
-            x[e] = (c * FE + e < P) ? A[r][e] * rl : 0.f;
-            n2 = fmaf(x[e], x[e], n2);
-          }
-          n2 = row16_sum(n2);
-          const float i1 = n2 > 0.f ? fast_rsq(n2) : 0.f;
-          const float n1 = n2 * i1;
-          float u[FE];
-#pragma unroll
-          for (int e = 0; e < FE; ++e) u[e] = x[e] * i1;
-          if (t >= 1) {
-            const float ds = fabsf(n1 - n0[r]);
-            float dd = INFINITY;
-            if (n1 > 0.f && n0[r] > 0.f) {
-              // 1 - cos as half the squared distance of the unit vectors
-              float u2 = 0.f;
-#pragma unroll
-              for (int e = 0; e < FE; ++e) {
-                const float du = u[e] - xp[r][e];
-                u2 = fmaf(du, du, u2);
-              }
-              dd = 0.5f * row16_sum(u2);
-            }
-            const bool stable = ds < p.tau && dd < p.phi;
-            cnt[r] = stable ? cnt[r] + 1 : 0;
-            if (cnt[r] >= p.patience) stopT[r] = t;
-          }
-#pragma unroll
-          for (int e = 0; e < FE; ++e) xp[r][e] = u[e];
-          n0[r] = n1;
-        }
-        if (stopT[r] < 0) live = true;
+        for (int e = 0; e < FE; ++e) A[r][e] = alr * A[r][e] + ber * a[r][e];
       }
     }
     if (lane == 0) st_rel(&sh.folded, t + 1);
-    if (__ballot(live) == 0) break;
+    if (__ballot(dec && dstop < 0) == 0) break;
   }
   if (lane == 0) st_rel(&sh.done, 1);
   // outputs: the frozen (or final) state of every head
 #pragma unroll
   for (int r = 0; r < GR; ++r) {
+    float Lr = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lj = readlane(dL, 4 * r + j);
+      Lr = q4 == j ? lj : Lr;
+    }
     const int q = 4 * r + q4;
     if (q < G) {
       float* dst = p.out + ((size_t)b * p.Hq + (size_t)g * G + q) * D + c * FE;
 #pragma unroll
-      for (int e = 0; e < FE; ++e) dst[e] = Ls[r] > 0.f ? A[r][e] / Ls[r] : 0.f;
-      if (c == 0)
-        p.stop_pos[(size_t)b * p.Hq + (size_t)g * G + q] = nb == 0 ? -1 : (stopT[r] >= 0 ? stopT[r] : nb - 1);
+      for (int e = 0; e < FE; ++e) dst[e] = Lr > 0.f ? A[r][e] / Lr : 0.f;
     }
   }
+  if (dec) p.stop_pos[(size_t)b * p.Hq + (size_t)g * G + lane] = nb == 0 ? -1 : (dstop >= 0 ? dstop : nb - 1);
 }
 
-template <typename T, int D, int GR, int NP, int R>
+template <typename T, int D, int GR, int NP, int R, bool PF>
 __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
-  using SH = ArtShared<T, D, GR, NP, R>;
+  using SH = ArtShared<T, D, GR, NP, R, PF>;
   __shared__ SH sh;
   const int unit = blockIdx.x;
   const int b = unit / p.Hkv, g = unit % p.Hkv;
@@ -331,8 +409,8 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
 
 // With at least one (b, kv head) unit per CU the chip is bandwidth-bound and
 // the 8-block read-ahead keeps over-fetch small; with fewer units each
-// workgroup must pull more bandwidth by itself, so it gets 15 producers and a
-// 16-block window.
+// workgroup must pull more bandwidth by itself, so its producers pipeline
+// their loads across positions within a 16-block window.
 template <typename T, int D>
 hipError_t launch_art_t(const ArtArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
@@ -343,11 +421,11 @@ hipError_t launch_art_t(const ArtArgs& a, hipStream_t st) {
     cus = 256;
   const dim3 grid(units);
   if (G > 4)
-    art_kernel<T, D, 2, 7, 8><<<grid, 8 * 64, 0, st>>>(a);
+    art_kernel<T, D, 2, 7, 8, false><<<grid, 8 * 64, 0, st>>>(a);
   else if (units >= cus)
-    art_kernel<T, D, 1, 7, 8><<<grid, 8 * 64, 0, st>>>(a);
+    art_kernel<T, D, 1, 7, 8, false><<<grid, 8 * 64, 0, st>>>(a);
   else
-    art_kernel<T, D, 1, 15, 16><<<grid, 16 * 64, 0, st>>>(a);
+    art_kernel<T, D, 1, 7, 16, true><<<grid, 8 * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -235,8 +235,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   for (int q = 0; q < GP; ++q)
 #pragma unroll
     for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int off = CPR; off < 64; off <<= 1) acc[q][e] += __shfl_xor(acc[q][e], off);
+      acc[q][e] = phase_sum<CPR>(acc[q][e]);
 
   if (arow == 0) {
 #pragma unroll

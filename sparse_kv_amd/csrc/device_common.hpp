@@ -71,18 +71,38 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-  x = row16_sum(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+// Sum of x over the lanes that differ only in lane bit 4 (resp. 5): with both
+// operands equal, permlane16_swap returns (even rows, odd rows) of 16 lanes
+// duplicated in place, permlane32_swap (low half, high half); the two halves'
+// sum is identical in every lane.  Pure VALU, no LDS traffic.
+__device__ __forceinline__ float xrow16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xrow16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-  x = row16_max(x);
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+__device__ __forceinline__ float wave_sum(float x) { return xhalf_sum(xrow16_sum(row16_sum(x))); }
+__device__ __forceinline__ float wave_max(float x) { return xhalf_max(xrow16_max(row16_max(x))); }
+
+// Sum over the lanes sharing lane % CPR (the token phases of the row layout):
+// lane bits log2(CPR) .. 5.
+template <int CPR>
+__device__ __forceinline__ float phase_sum(float x) {
+  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "chunks per row");
+  if constexpr (CPR == 8) x += dpp<0x128>(x);  // row_ror:8 pairs lane l with l ^ 8
+  if constexpr (CPR <= 16) x = xrow16_sum(x);
+  return xhalf_sum(x);
 }
 
 __device__ __forceinline__ float readlane(float x, int lane) {

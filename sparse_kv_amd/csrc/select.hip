@@ -53,8 +53,7 @@ __global__ __launch_bounds__(256) void centroid_kernel(const void* __restrict__ 
   }
 #pragma unroll
   for (int e = 0; e < E; ++e)
-#pragma unroll
-    for (int off = CPR; off < 64; off <<= 1) sum[e] += __shfl_xor(sum[e], off);
+    sum[e] = phase_sum<CPR>(sum[e]);
   const float n = (float)min(kBlock, L - j * kBlock);
   if (lane < CPR) {
 #pragma unroll
@@ -101,7 +100,7 @@ __global__ __launch_bounds__(256) void score_kernel(const void* __restrict__ q, 
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     float s = row16_sum(part[it]);
-    if constexpr (LPR == 32) s += __shfl_xor(s, 16);
+    if constexpr (LPR == 32) s = xrow16_sum(s);
     const int j = j0 + it * RPI + lane / LPR;
     if (c == 0 && j < NBmax) srow[j] = j < nb ? s * scale : -INFINITY;
   }
