@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", default="dense,sparse,art,window")
+    ap.add_argument("--splits-per-shard", type=int, default=4, help="hybrid256k: inner splits per context shard")
+    ap.add_argument("--sa-splits", type=int, default=32, help="hybrid256k: splits of a sink+window layer")
     ap.add_argument("--workload", default="decode128k", choices=["decode128k", "art64k", "hybrid256k"],
                     help="decode128k (default): the 128K batch-8 step above; art64k: ART on the 64K batch-32 "
                          "recency workload vs dense; hybrid256k: 36-layer routed stack at 256K vs all-full")
@@ -387,8 +389,9 @@ def bench_hybrid256k(args):
     print(f"[bench] generated 36 layers in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
     sa_idx, sa_n = skv.attn_select_topk(None, None, k=0, n_sink_blocks=W["n_sink"], n_recent_blocks=W["n_recent"],
                                         shape=(B, Hkv, nb), device=dev)
-    kw = dict(n_shards=W["n_shards"], splits_per_shard=32, sa_block_idx=sa_idx, sa_n_sel=sa_n, sa_splits=8)
-    ws = torch.empty(skv.attn_routed_workspace_bytes(qs[0], ks[0], W["n_shards"], 32, 8), dtype=torch.uint8,
+    sps, sas = args.splits_per_shard, args.sa_splits
+    kw = dict(n_shards=W["n_shards"], splits_per_shard=sps, sa_block_idx=sa_idx, sa_n_sel=sa_n, sa_splits=sas)
+    ws = torch.empty(skv.attn_routed_workspace_bytes(qs[0], ks[0], W["n_shards"], sps, sas), dtype=torch.uint8,
                      device=dev)
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in qs]
     th, tf = _timer(), _timer()
@@ -406,8 +409,9 @@ def bench_hybrid256k(args):
     by_f = len(mask) * B * Hkv * nb * kv_block + len(mask) * B * Hq * d * 6
     _line(args, "routed hybrid decode HBM GB/s, 36 layers, 256K ctx, batch 1", by / (ms_h * 1e-3) / 1e9, "GB/s",
           ms_h, {"workload": "one decode step through a 36-layer routed stack (18 full / 18 sink+window), "
-                             "256K context, batch 1, 32 q / 8 kv heads, d 128, bf16 KV; full layers as 8 "
-                             "context shards x 32 splits", "batch": B, "context": L, "parallelism": "single-gpu"},
+                             f"256K context, batch 1, 32 q / 8 kv heads, d 128, bf16 KV; full layers as 8 "
+                             f"context shards x {sps} splits", "batch": B, "context": L, "splits_per_shard": sps,
+                             "sa_splits": sas, "parallelism": "single-gpu"},
           tokens_per_s=round(B / (ms_h * 1e-3), 2), all_full_ms=round(ms_f, 4),
           all_full_gbs=round(by_f / (ms_f * 1e-3) / 1e9, 1), speedup_vs_all_full=round(ms_f / ms_h, 3),
           byte_ratio=round(by_f / by, 3))

@@ -29,6 +29,10 @@
 //     range check covers); their logits are masked to -inf.
 // At the end the 4 waves' states are merged through LDS and the split's
 // (m, l, o) is written, o normalised, m in natural-log units.
+// Measured on MI355X at 128K context, batch 8: 6.93 TB/s with the pipelined
+// loop (the compiler then keeps one workgroup per CU) against 6.86 TB/s for
+// the plain loop at 2-3 workgroups per CU, which also re-fetches ~2% of K
+// from HBM because more half-read K lines are evicted from L2 in between.
 #include "device_common.hpp"
 #include "kernels.hpp"
 

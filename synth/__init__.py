@@ -225,5 +225,5 @@ WORKLOADS = {
             kind="recency", tau=1e-3, phi=1e-4, patience=2, probe_dim=8),
     5: dict(name="qwen3-8b 36-layer routed hybrid 256K b1", B=1, Hq=32, Hkv=8, d=128,
             L=262144, dtype="bf16", kind="needles", n_layers=36, n_full=18, n_shards=8,
-            n_sink=1, n_recent=128),
+            splits_per_shard=4, sa_splits=32, n_sink=1, n_recent=128),
 }

@@ -137,8 +137,9 @@ def test_routed_36_layer_stack_256k():
     log(f"[full] 36-layer 256K stack: inputs in {time.time() - t:.1f}s")
     sa_idx, sa_n = skv.attn_select_topk(None, None, k=0, n_sink_blocks=W["n_sink"], n_recent_blocks=W["n_recent"],
                                         shape=(B, Hkv, nb), device="cuda")
-    outs = skv.attn_decode_routed(qs, ks, vs, mask, None, n_shards=W["n_shards"], splits_per_shard=32,
-                                  sa_block_idx=sa_idx, sa_n_sel=sa_n, sa_splits=8)
+    # the benchmark's launch configuration: 8 shards x 4 splits, 32 splits for sink + window layers
+    outs = skv.attn_decode_routed(qs, ks, vs, mask, None, n_shards=W["n_shards"], splits_per_shard=4,
+                                  sa_block_idx=sa_idx, sa_n_sel=sa_n, sa_splits=32)
     torch.cuda.synchronize()
     G = Hq // Hkv
     for i in sorted(check):
