@@ -42,7 +42,7 @@ from .attention import (
     decode_sparse_split_states,
 )
 from .selection import block_centroids, centroid_scores, select_blocks, select_all
-from .art import probe_metrics, art_decode_head, art_decode, default_order
+from .art import probe_metrics, art_decode_head, art_decode, default_order, importance_order
 from .routing import routed_layer_outputs
 
 __all__ = [
@@ -63,5 +63,6 @@ __all__ = [
     "art_decode_head",
     "art_decode",
     "default_order",
+    "importance_order",
     "routed_layer_outputs",
 ]

@@ -9,7 +9,10 @@ paper 2606.00024):
   in a visit order; after t+1 blocks the partial output O^(t) is available.
 * §2.4: the visit order may be re-arranged ("recency first" or "importance
   first"); the first block (block 0, the attention sink) is always evaluated
-  before any early exit.  Default order here: (0, nb-1, nb-2, ..., 1).
+  before any early exit.  Default order here: (0, nb-1, nb-2, ..., 1);
+  importance first: block 0, then descending centroid score.  ART composes
+  with KV selection (§2.4, orthogonal control layer): the visit order may
+  list only some blocks, and then attention is over those blocks.
 * §2.2: a small probe vector x^(t) is read from the partial output.  Reading:
   x^(t) = the first ``probe_dim`` channels of the normalised partial output
   (the output if attention stopped now).  Two changes are measured against
@@ -52,6 +55,16 @@ def default_order(nb: int):
     return [0] + list(range(nb - 1, 0, -1))
 
 
+def importance_order(scores_row, nb: int):
+    """Block 0 first, then the other blocks by descending score ("importance
+    first", ART summary §2.4), lower index first among equal float32 scores."""
+    if nb <= 0:
+        return []
+    s32 = np.asarray(scores_row, dtype=np.float64)[:nb].astype(np.float32)
+    rest = sorted(range(1, nb), key=lambda j: (-float(s32[j]), j))
+    return [0] + rest
+
+
 def probe_metrics(x_cur, x_prev):
     """(d_scale, d_dir) between two probe vectors; d_dir = inf if a norm is 0."""
     n1 = math.sqrt(float(np.dot(x_cur, x_cur)))
@@ -72,21 +85,22 @@ def art_decode_head(q, K, V, L: int, scale: float, order, tau: float, phi: float
                     patience: int, probe_dim: int, block: int = 64):
     """ART for one query head over one KV head.
 
-    q [d]; K, V [Lmax, d] float64; ``order``: visit order of the nb blocks
-    (starting with 0).  Returns (O [d], T, trace) where T is the visit position
-    of the last folded block (-1 for an empty sequence) and trace lists
-    (t, d_scale, d_dir, stable, counter) for every compared step.
+    q [d]; K, V [Lmax, d] float64; ``order``: the visit order, distinct blocks
+    of the sequence starting with 0 -- all nb of them, or fewer to visit only
+    those (ART over a selected list).  Returns (O [d], T, trace) where T is the
+    visit position of the last folded block (-1 when nothing is visited) and
+    trace lists (t, d_scale, d_dir, stable, counter) for every compared step.
     """
     d = q.shape[-1]
     nb = num_blocks(L, block)
-    if nb == 0:
-        return np.zeros(d), -1, []
     order = list(order)[:nb]
+    if not order:
+        return np.zeros(d), -1, []
     state = (-math.inf, 0.0, np.zeros(d))
     x_prev = None
     counter = 0
     trace = []
-    T = nb - 1
+    T = len(order) - 1
     for t, j in enumerate(order):
         lo, hi = j * block, min((j + 1) * block, L)
         state = merge_states([state, head_state(q, K[lo:hi], V[lo:hi], scale)], d)
@@ -106,8 +120,10 @@ def art_decode_head(q, K, V, L: int, scale: float, order, tau: float, phi: float
 
 
 def art_decode(q, k, v, seq_lens, scale: float, tau: float, phi: float, patience: int,
-               probe_dim: int, order=None, block: int = 64):
-    """ART for every (b, h).  order: None (default order) or int [B, Hkv, NBmax].
+               probe_dim: int, order=None, n_visit=None, block: int = 64):
+    """ART for every (b, h).  order: None (default order) or int [B, Hkv, NBmax];
+    n_visit: None (visit nb blocks) or int [B, Hkv] (visit only the first
+    n_visit entries of the order).
 
     Returns (out [B, Hq, d], stop [B, Hq] int, traces dict (b, h) -> trace).
     """
@@ -123,6 +139,8 @@ def art_decode(q, k, v, seq_lens, scale: float, tau: float, phi: float, patience
         for h in range(Hq):
             g = h // G
             ordr = default_order(nb) if order is None else [int(x) for x in order[b][g][:nb]]
+            if n_visit is not None:
+                ordr = ordr[:max(0, min(int(n_visit[b][g]), nb))]
             O, T, tr = art_decode_head(q[b, h], k[b, g], v[b, g], L, scale, ordr, tau, phi,
                                        patience, probe_dim, block)
             out[b, h], stop[b, h], traces[(b, h)] = O, T, tr

@@ -105,3 +105,35 @@ def test_margin_helper():
     assert art_margin_ok(tr, 1e-3, 1e-4)
     assert not art_margin_ok([(1, 0.995e-3, 5e-5, True, 1)], 1e-3, 1e-4)
     assert not art_margin_ok([(1, 1.005e-3, 5e-5, False, 0)], 1e-3, 1e-4)
+
+
+def test_importance_order():
+    s = np.array([9.0, 1.0, 3.0, 3.0, -2.0, 7.0, 3.0])
+    # block 0 first whatever its score, then descending score, ties to the lower index
+    assert oracle.importance_order(s, 7) == [0, 5, 2, 3, 6, 1, 4]
+    assert oracle.importance_order(s, 1) == [0]
+    assert oracle.importance_order(s, 0) == []
+    r = np.random.default_rng(4)
+    x = r.standard_normal(50)
+    o = oracle.importance_order(x, 50)
+    assert o[0] == 0 and sorted(o) == list(range(50))
+    assert all(np.float32(x[a]) >= np.float32(x[b]) for a, b in zip(o[1:], o[2:]))
+
+
+def test_art_over_a_listed_subset():
+    # visiting only listed blocks: with tau = phi = 0 it is attention over those blocks
+    q, k, v, seq = inputs(6)
+    lst = [0, 7, 3, 9]
+    out, stop, _ = art_decode(q, k, v, seq, 0.25, 0.0, 0.0, 1, 8, order=[[lst]], n_visit=[[4]], block=8)
+    assert (stop == 3).all()
+    ref = oracle.decode_blocks(q, k, v, seq, 0.25, [[sorted(lst)]], block=8)
+    assert np.max(np.abs(out - ref)) < 1e-12
+    # n_visit = 0 visits nothing
+    out, stop, _ = art_decode(q, k, v, seq, 0.25, 0.0, 0.0, 1, 8, order=[[lst]], n_visit=[[0]], block=8)
+    assert (stop == -1).all() and not out.any()
+    # a stop inside the list: tau = phi = inf, p = 1 stops at the second listed block
+    out, stop, _ = art_decode(q, k, v, seq, 0.25, math.inf, math.inf, 1, 8, order=[[lst]], n_visit=[[4]], block=8)
+    assert (stop == 1).all()
+    toks = list(range(0, 8)) + list(range(56, 64))
+    ref = brute.attention_over_tokens(list(q[0, 0]), k[0, 0], v[0, 0], toks, 0.25)
+    assert np.max(np.abs(out[0, 0] - np.array(ref))) < 1e-12
