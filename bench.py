@@ -10,6 +10,8 @@ One timed step runs every stage of the hot path over that batch:
   sparse  centroid scores + top-k (10% + sink + last 64) + listed-block decode + merge
   art     ART early-terminated decode, block 0 then most recent first
   window  sink + recent-window decode + merge                 (routed SA layer)
+Optional (--stages ...,art_imp): centroid scores + importance order + ART
+visiting block 0 then blocks by descending centroid score.
 Block centroids are built once before timing (they change only when a block
 fills).  Each stage reads its own copy of the KV cache so that no stage is
 served from the 256 MB last-level cache filled by the previous one.
@@ -69,7 +71,8 @@ def parse():
     ap.add_argument("--window-splits", type=int, default=4, help="splits per unit, sink+window stage")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stages", default="dense,sparse,art,window")
+    ap.add_argument("--stages", default="dense,sparse,art,window",
+                    help="comma list of dense, sparse, art, window, art_imp")
     ap.add_argument("--splits-per-shard", type=int, default=4, help="hybrid256k: inner splits per context shard")
     ap.add_argument("--sa-splits", type=int, default=32, help="hybrid256k: splits of a sink+window layer")
     ap.add_argument("--workload", default="decode128k", choices=["decode128k", "art64k", "hybrid256k"],
@@ -117,15 +120,17 @@ def main():
     q = up(inp.q)
     copies = {}
     k0, v0 = up(inp.k), up(inp.v)
-    for i, s in enumerate(("dense", "sparse", "art", "window")):
-        copies[s] = (k0, v0) if i == 0 else (k0.clone(), v0.clone())
+    for i, s in enumerate(("dense", "sparse", "art", "window", "art_imp")):
+        if s in stages or s == "dense":
+            copies[s] = (k0, v0) if i == 0 else (k0.clone(), v0.clone())
     torch.cuda.synchronize()
 
     # prefill-time work: centroids of the sparse stage's cache, the window list
     c_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     c_ev[0].record()
-    C = skv.attn_build_centroids(copies["sparse"][0])
+    C = skv.attn_build_centroids(copies["sparse"][0]) if "sparse" in stages else None
     c_ev[1].record()
+    C_imp = skv.attn_build_centroids(copies["art_imp"][0]) if "art_imp" in stages else None
     win_idx, win_n = skv.attn_select_topk(None, None, k=0, n_sink_blocks=n_sink, n_recent_blocks=win_recent,
                                           shape=(B, Hkv, NB), device=dev)
     torch.cuda.synchronize()
@@ -143,6 +148,11 @@ def main():
     sel_n = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
     stop = torch.empty((B, Hq), dtype=torch.int32, device=dev)
     fetched = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    scores_i = torch.empty((B, Hkv, NB), **f32)
+    order_i = torch.empty((B, Hkv, NB), dtype=torch.int32, device=dev)
+    out_i = torch.empty((B, Hq, d), **f32)
+    stop_i = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    fetched_i = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
 
     names = ["dense_kernel", "dense_merge", "sparse", "art", "window"]
     ev = {}
@@ -182,6 +192,16 @@ def main():
             skv.attn_decode_sparse(q, kw, vw, win_idx, win_n, None, num_splits=Sw, m=st_w[0], l=st_w[1], o=st_w[2])
             skv.attn_merge_states(*st_w, out=out_w)
             mark("window.1")
+        if "art_imp" in stages:
+            ki, vi = copies["art_imp"]
+            mark("art_imp.0")
+            skv.attn_score_centroids(q, C_imp, None, out=scores_i)
+            mark("art_imp.score")
+            skv.attn_order_blocks(scores_i, None, out=order_i)
+            mark("art_imp.order")
+            skv.attn_decode_art(q, ki, vi, None, order=order_i, tau=tau, phi=phi, patience=patience,
+                                probe_dim=probe, out=out_i, stop_pos=stop_i, blocks_fetched=fetched_i)
+            mark("art_imp.1")
 
     for _ in range(args.warmup):
         step(False)
@@ -235,8 +255,27 @@ def main():
         by = float(win_n.cpu().numpy().sum()) * kv_block + q_bytes + o_bytes
         total_bytes += by
         paths["window"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), tokens_per_s=B / (ms * 1e-3), splits=Sw)
+    if "art_imp" in stages:
+        stp = stop_i.cpu().numpy().reshape(B, Hkv, Hq // Hkv)
+        need = stp.max(axis=2) + 1
+        ms = avg_ms("art_imp.0", "art_imp.1")
+        by = (float(need.sum()) * kv_block + units * NB * d * 4 + units * NB * 4 * 2 + units * NB * 4
+              + float(need.sum()) * 4 + q_bytes + o_bytes)
+        total_bytes += by
+        paths["art_imp"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), score_ms=avg_ms("art_imp.0", "art_imp.score"),
+                                order_ms=avg_ms("art_imp.score", "art_imp.order"),
+                                art_ms=avg_ms("art_imp.order", "art_imp.1"), mean_stop=float(stp.mean()),
+                                blocks_needed_per_unit=float(need.mean()),
+                                blocks_fetched_per_unit=float(fetched_i.cpu().numpy().mean()),
+                                tokens_per_s=B / (ms * 1e-3))
+        if "dense" in stages:
+            # accuracy against full attention, recency-first and importance-first
+            ref = out_d.double()
+            paths["art_imp"]["max_abs_err_vs_dense"] = float((out_i.double() - ref).abs().max())
+            if "art" in stages:
+                paths["art"]["max_abs_err_vs_dense"] = float((out_a.double() - ref).abs().max())
     if "dense" in paths:
-        for k_ in ("sparse", "art", "window"):
+        for k_ in ("sparse", "art", "window", "art_imp"):
             if k_ in paths:
                 paths[k_]["speedup_vs_dense"] = paths["dense"]["ms"] / paths[k_]["ms"]
 

@@ -176,12 +176,50 @@ int attn_decode_sparse(const attn_dims* dims, const void* q, const void* k, cons
  *                   (>= max over the group of T + 1; speculative read-ahead
  *                   beyond the stop is counted).
  * probe_dim = 0 turns the detector off (dense result, T = nb - 1).
- * Requires patience >= 1, 0 <= probe_dim <= min(d, 64), tau, phi not NaN.
+ * Requires patience >= 1, probe_dim >= 0, tau, phi not NaN (else
+ * ATTN_ERR_INVALID_ARG); probe_dim > min(d, 16) is ATTN_ERR_UNSUPPORTED.
  */
 int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const void* v,
                     const int32_t* seq_lens, const int32_t* order, float tau, float phi,
                     int32_t patience, int32_t probe_dim, float* out, int32_t* stop_pos,
                     int32_t* blocks_fetched, void* stream);
+
+/*
+ * ART over a listed subset of blocks.
+ * Defines: "ART (Attention Run-time Termination)" summary, §2.4 -- the stop
+ * rule is a control layer that composes with KV selection: the visit order
+ * is the list, and attention is over the listed blocks folded so far.
+ *   block_list  int32 [B, Hkv, max_list], n_list int32 [B, Hkv]: per (b, g)
+ *               the first n = clamp(n_list, 0, min(max_list, nb(b))) entries
+ *               are visited in list order; they must be distinct blocks
+ *               < nb(b), block 0 first when the sink is kept (precondition;
+ *               entries are clamped into [0, nb)).  An attn_select_topk result
+ *               (ascending, sink first) or a prefix of attn_order_blocks
+ *               output with max_list = max_blocks both qualify.
+ * Stop rule, out, stop_pos and blocks_fetched as in attn_decode_art with nb
+ * replaced by n: with no stop T = n - 1; n = 0 gives zeros and T = -1.
+ */
+int attn_decode_art_list(const attn_dims* dims, const void* q, const void* k, const void* v,
+                         const int32_t* seq_lens, const int32_t* block_list, const int32_t* n_list,
+                         int32_t max_list, float tau, float phi, int32_t patience, int32_t probe_dim,
+                         float* out, int32_t* stop_pos, int32_t* blocks_fetched, void* stream);
+
+/*
+ * Importance-first visit order from block scores.
+ * Defines: "ART (Attention Run-time Termination)" summary, §2.4 (the visit
+ * order may put the most important blocks first; the first block is always
+ * evaluated first), with importance = the centroid score of
+ * attn_score_centroids ("Squeezed Attention" blog, Q2 step 2).
+ *   scores  float [B, Hkv, max_blocks] (finite for blocks < nb(b)).
+ *   order   int32 [B, Hkv, max_blocks] out: 0, then blocks 1 .. nb-1 by
+ *           descending float32 score, lower index first among equal scores
+ *           (-0 equals +0); -1 from position nb on.  Usable as the order of
+ *           attn_decode_art.
+ * Supports max_blocks - 1 <= 16384 (1M tokens at 64 per block), else
+ * ATTN_ERR_UNSUPPORTED.
+ */
+int attn_order_blocks(const attn_dims* dims, const float* scores, const int32_t* seq_lens,
+                      int32_t* order, void* stream);
 
 /*
  * One decode step of a layer stack under a per-layer hard route.

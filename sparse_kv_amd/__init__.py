@@ -32,6 +32,8 @@ EXPORTS = (
     "attn_select_topk",
     "attn_decode_sparse",
     "attn_decode_art",
+    "attn_decode_art_list",
+    "attn_order_blocks",
     "attn_decode_routed",
     "attn_routed_workspace_bytes",
     "attn_status_string",
@@ -63,6 +65,8 @@ _SIG = {
     "attn_select_topk": [_D, _P, _P, _I, _I, _I, _I, _P, _P, _P],
     "attn_decode_sparse": [_D, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P],
     "attn_decode_art": [_D, _P, _P, _P, _P, _P, _F, _F, _I, _I, _P, _P, _P, _P],
+    "attn_decode_art_list": [_D, _P, _P, _P, _P, _P, _P, _I, _F, _F, _I, _I, _P, _P, _P, _P],
+    "attn_order_blocks": [_D, _P, _P, _P, _P],
     "attn_decode_routed": [_D, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _P, ctypes.c_size_t, _P, _P],
     "attn_routed_workspace_bytes": [_D, _I, _I, _I],
 }
@@ -345,6 +349,47 @@ def attn_decode_art(q, k, v, seq_lens=None, order=None, tau=1e-3, phi=1e-4, pati
                                   _ptr(stop_pos), _ptr(blocks_fetched), _stream(dev))
     _check(st, "attn_decode_art")
     return out, stop_pos, blocks_fetched
+
+
+def attn_decode_art_list(q, k, v, block_list, n_list, seq_lens=None, tau=1e-3, phi=1e-4, patience=2,
+                         probe_dim=8, scale=None, out=None, stop_pos=None, blocks_fetched=None):
+    """ART over listed blocks, visited in list order: same outputs as attn_decode_art."""
+    dev = q.device
+    dims = _dims_from(q, k, scale)
+    _need(q, "q", dev)
+    _need(k, "k", dev)
+    _need(v, "v", dev, k.dtype, k.shape)
+    _need(block_list, "block_list", dev, torch.int32)
+    if block_list.dim() != 3 or tuple(block_list.shape[:2]) != (dims.batch, dims.num_kv_heads):
+        raise ValueError("block_list must be [B, Hkv, max_list]")
+    _need(n_list, "n_list", dev, torch.int32, (dims.batch, dims.num_kv_heads))
+    seq = _seq(seq_lens, dims.batch, dev)
+    out = _out(out, (dims.batch, dims.num_q_heads, dims.head_dim), torch.float32, dev, "out")
+    stop_pos = _out(stop_pos, (dims.batch, dims.num_q_heads), torch.int32, dev, "stop_pos")
+    blocks_fetched = _out(blocks_fetched, (dims.batch, dims.num_kv_heads), torch.int32, dev, "blocks_fetched")
+    with _on_device(dev):
+        st = lib().attn_decode_art_list(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(seq),
+                                       _ptr(block_list), _ptr(n_list), int(block_list.shape[2]),
+                                       float(tau), float(phi), int(patience), int(probe_dim), _ptr(out),
+                                       _ptr(stop_pos), _ptr(blocks_fetched), _stream(dev))
+    _check(st, "attn_decode_art_list")
+    return out, stop_pos, blocks_fetched
+
+
+def attn_order_blocks(scores, seq_lens=None, out=None):
+    """Importance-first visit order [B, Hkv, NBmax] int32 from block scores [B, Hkv, NBmax]."""
+    dev = scores.device
+    _need(scores, "scores", dev, torch.float32)
+    if scores.dim() != 3:
+        raise ValueError("scores must be [B, Hkv, NBmax]")
+    B, Hkv, NBmax = scores.shape
+    dims = AttnDims(B, Hkv, Hkv, 64, BLOCK, NBmax, ATTN_F32, 1.0)
+    seq = _seq(seq_lens, B, dev)
+    out = _out(out, (B, Hkv, NBmax), torch.int32, dev, "out")
+    with _on_device(dev):
+        st = lib().attn_order_blocks(ctypes.byref(dims), _ptr(scores), _ptr(seq), _ptr(out), _stream(dev))
+    _check(st, "attn_order_blocks")
+    return out
 
 
 def attn_routed_workspace_bytes(q, k, n_shards=8, splits_per_shard=4, sa_splits=4, scale=None):

@@ -182,10 +182,11 @@ int attn_decode_sparse(const attn_dims* dims, const void* q, const void* k, cons
   return hip_status(skv::launch_decode(a, true, (hipStream_t)stream));
 }
 
-int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const void* v,
-                    const int32_t* seq_lens, const int32_t* order, float tau, float phi,
-                    int32_t patience, int32_t probe_dim, float* out, int32_t* stop_pos,
-                    int32_t* blocks_fetched, void* stream) {
+static int art_common(const attn_dims* dims, const void* q, const void* k, const void* v,
+                      const int32_t* seq_lens, const int32_t* order, int32_t order_stride,
+                      const int32_t* n_visit, float tau, float phi, int32_t patience,
+                      int32_t probe_dim, float* out, int32_t* stop_pos, int32_t* blocks_fetched,
+                      void* stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!q || !k || !v || !out || !stop_pos) return ATTN_ERR_INVALID_ARG;
@@ -199,6 +200,8 @@ int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const v
   a.v = v;
   a.seq_lens = seq_lens;
   a.order = order;
+  a.order_stride = order_stride;
+  a.n_visit = n_visit;
   a.tau = tau;
   a.phi = phi;
   a.patience = patience;
@@ -214,6 +217,35 @@ int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const v
   a.dtype = dims->dtype;
   a.scale = dims->scale;
   return hip_status(skv::launch_art(a, (hipStream_t)stream));
+}
+
+int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const void* v,
+                    const int32_t* seq_lens, const int32_t* order, float tau, float phi,
+                    int32_t patience, int32_t probe_dim, float* out, int32_t* stop_pos,
+                    int32_t* blocks_fetched, void* stream) {
+  const int32_t stride = dims ? dims->max_blocks : 0;
+  return art_common(dims, q, k, v, seq_lens, order, stride, nullptr, tau, phi, patience, probe_dim,
+                    out, stop_pos, blocks_fetched, stream);
+}
+
+int attn_decode_art_list(const attn_dims* dims, const void* q, const void* k, const void* v,
+                         const int32_t* seq_lens, const int32_t* block_list, const int32_t* n_list,
+                         int32_t max_list, float tau, float phi, int32_t patience, int32_t probe_dim,
+                         float* out, int32_t* stop_pos, int32_t* blocks_fetched, void* stream) {
+  if (!block_list || !n_list || max_list < 1) return ATTN_ERR_INVALID_ARG;
+  return art_common(dims, q, k, v, seq_lens, block_list, max_list, n_list, tau, phi, patience,
+                    probe_dim, out, stop_pos, blocks_fetched, stream);
+}
+
+int attn_order_blocks(const attn_dims* dims, const float* scores, const int32_t* seq_lens,
+                      int32_t* order, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!scores || !order) return ATTN_ERR_INVALID_ARG;
+  if (dims->max_blocks - 1 > skv::kOrderMaxRest) return ATTN_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return ATTN_OK;
+  return hip_status(skv::launch_order(scores, seq_lens, dims->batch, dims->num_kv_heads,
+                                      dims->max_blocks, order, (hipStream_t)stream));
 }
 
 size_t attn_routed_workspace_bytes(const attn_dims* dims, int32_t n_shards, int32_t splits_per_shard,

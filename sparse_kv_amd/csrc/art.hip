@@ -9,18 +9,19 @@
 //
 // One workgroup = one (b, kv head), split by role:
 //   * 7 producer waves stream blocks: producer i takes visit positions
-//     i, i+7, i+14, ... (loads software-pipelined across positions when the
-//     grid has fewer units than CUs); for each it loads the block (16-byte buffer loads),
+//     i, i+7, i+14, ...; for each it loads the block (16-byte buffer loads),
 //     forms the G x 64 logits on MFMA, the block-local softmax, and P.V in
 //     fp32, and publishes the block's state (m, l, unnormalised P.V of all
-//     channels) into an R-slot ring in LDS (R = 8, or 16 when pipelined).
+//     channels) into an R-slot ring in LDS (R = 8 when every CU has a unit,
+//     else 16).
 //   * 1 folder wave folds the published states strictly in visit order into
-//     the running state -- the exact sequence of a one-block-at-a-time
-//     streaming kernel -- and after every fold evaluates the stop rule per
-//     query head on the probe channels (one decision lane per head, so the
-//     serial chain has no cross-lane reductions).  A head
-//     that stops freezes its state; when every head of the group has
-//     stopped (or the blocks run out) the folder writes the outputs.
+//     the running state -- the result of a one-block-at-a-time streaming
+//     kernel -- a batch of consecutive published positions at a time, and
+//     evaluates the stop rule per query head at every position of the batch.
+//     A head that stops freezes its state; when every head of the group has
+//     stopped (or the positions run out) the folder writes the outputs.
+// Visit positions come from the default order, an explicit order, or a
+// list of blocks (ART over a selection, §2.4), optionally cut to a count.
 // Ring protocol (acquire/release on LDS words): a producer may start
 // position t only once position t-R has been folded, so read-ahead past the
 // final stop is at most R blocks (counted in blocks_fetched); the folder
@@ -41,30 +42,30 @@ __device__ __forceinline__ void st_rel(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// NP producer waves, R ring slots (R also bounds the read-ahead), PF: producers
-// software-pipeline their loads across positions.
-template <typename T, int D, int GR, int NP, int R, bool PF>
+// NP producer waves, R ring slots (R also bounds the read-ahead).
+template <typename T, int D, int GR, int NP, int R>
 struct ArtShared {
   static constexpr int GP = 4 * GR;
   static constexpr int kNP = NP, kR = R;
-  static constexpr bool kPF = PF;
   float p_lds[NP][64 * GP];
   float slot_acc[R][GP][D];
   float slot_m[R][GP];
   float slot_l[R][GP];
   int slot_pos[R];
+  float fold_w[64];  // per (head, batch position) output weights
+  float fold_a[GP];  // per head rescale of the running output
   int folded;
   int done;
   int fetched;
 };
 
-// Producer wave pi: visit positions pi, pi + NP, ...  With SH::kPF the loads
-// are software-pipelined as in the split-KV kernel: the next position's K is
-// requested right after this block's logits and its V right after this
-// block's P.V (when the read-ahead window already allows it), so HBM latency
-// hides behind this block's arithmetic with no extra registers.
+// Producer wave pi: visit positions pi, pi + NP, ...  Each block is loaded
+// whole (K in the MFMA operand layout, V in the row layout) before its
+// logits, softmax and P.V; with NP producers per workgroup, NP blocks are in
+// flight per CU.
 template <typename T, int D, int GR, typename SH>
-__device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, int g, int G, int L, int nb) {
+__device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, int g, int G, int L, int nb,
+                             int nv) {
   using Gm = Geo<T, D>;
   constexpr int GP = 4 * GR;
   constexpr int E = Gm::E, CPR = Gm::CPR, TPI = Gm::TPI, KA = Gm::KA, ROWB = Gm::ROWB;
@@ -92,9 +93,11 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
   const int phase = lane / CPR;
   float* pl = sh.p_lds[pi];
 
-  auto block_of = [&](int t) {
-    return p.order ? clampi(p.order[(size_t)unit * NBmax + t], 0, nb - 1) : (t == 0 ? 0 : nb - t);
-  };
+  // visit position -> block.  An explicit order's entry for the next position
+  // is read one block ahead, behind that block's K/V loads, so waiting for it
+  // never waits for loads still in flight.
+  auto order_at = [&](int t) { return (p.order && t < nv) ? p.order[(size_t)unit * p.order_stride + t] : 0; };
+  auto block_from = [&](int t, int o) { return p.order ? clampi(o, 0, nb - 1) : (t == 0 ? 0 : nb - t); };
   // read-ahead window: position t may start once t - kR has been folded
   auto window_open = [&](int t) { return ld_acq(&sh.folded) > t - kR; };
   auto window_wait = [&](int t) {
@@ -105,9 +108,6 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
     }
   };
   u32x4 kr[4][KA], vr[CPR];
-  // soff = byte offset of a block, or kNoBlock: past the buffers' range limit
-  // (slices are at most 2 GiB), so the loads return zeros and touch no memory
-  constexpr uint32_t kNoBlock = 0x80000000u;
   auto load_k = [&](uint32_t soff) {
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
@@ -124,8 +124,8 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
   };
 
   int t = pi;
-  if (t >= nb || !window_wait(t)) return;
-  int j = block_of(t);
+  if (t >= nv || !window_wait(t)) return;
+  int j = block_from(t, order_at(t));
   {
     const uint32_t so = block_off(j);
     load_k(so);
@@ -133,6 +133,7 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
   }
   while (true) {
     const int tn = t + kNP;
+    int onext = order_at(tn);
     f32x4 sc[4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
@@ -148,19 +149,6 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
         }
       }
       sc[t4] = c;
-    }
-    bool pf = false;
-    int jn = 0;
-    uint32_t son = kNoBlock;
-    if constexpr (SH::kPF) {
-      // unconditional loads keep one register lifetime; a closed window
-      // aims them past the range limit
-      pf = tn < nb && !ld_acq(&sh.done) && window_open(tn);
-      if (pf) {
-        jn = block_of(tn);
-        son = block_off(jn);
-      }
-      load_k(son);
     }
     const int nvalid = min(kBlock, L - j * kBlock);
     float mb[GR], lb[GR];
@@ -184,6 +172,7 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
       mb[r] = mx;
       lb[r] = row16_sum(ps);
     }
+    wave_lds_exchange();  // P rows written above are read across lanes below
     float ab[GP][E];
 #pragma unroll
     for (int q = 0; q < GP; ++q)
@@ -217,7 +206,7 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
 #pragma unroll
         for (int e = 0; e < E; ++e) ab[q][e] = fmaf(pq[q], vf[e], ab[q][e]);
     }
-    if constexpr (SH::kPF) load_v(son);
+    wave_lds_exchange();  // before the next block overwrites P
     // sum the token phases, publish the block state, then its position
 #pragma unroll
     for (int q = 0; q < GP; ++q)
@@ -239,147 +228,229 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
     }
     if (lane == 0) st_rel(&sh.slot_pos[s], t);
 
-    if (tn >= nb) return;
-    if (!pf) {
-      if (!window_wait(tn)) return;
-      jn = block_of(tn);
-      const uint32_t so = block_off(jn);
-      load_k(so);
-      load_v(so);
-    }
+    if (tn >= nv) return;
+    if (!window_wait(tn)) return;
+    asm volatile("" : "+v"(onext));  // keeps the wait for it here, after this block's K/V are used
+    j = block_from(tn, onext);
+    const uint32_t so = block_off(j);
+    load_k(so);
+    load_v(so);
     t = tn;
-    j = jn;
   }
 }
 
-// The folder wave.  Lane q < G is the decision lane of query head q: it keeps
-// that head's running max and denominator and the probe channels of its
-// running output, and evaluates the stop rule with no cross-lane traffic.
-// Every lane (row q % 4, channels c * FE ..) also folds its slice of the full
-// running output with the decision lanes' rescale factors, read back with
-// readlane; a head stops contributing after its stop position.
-template <typename T, int D, int GR, typename SH>
-__device__ void art_folder(const ArtArgs& p, SH& sh, int b, int g, int G, int nb) {
-  constexpr int FE = D / 16;  // output channels per lane
-  constexpr int PW = 16;      // probe channels a decision lane can hold (probe_dim <= 16)
-  constexpr int kR = SH::kR;
-  const int lane = threadIdx.x & 63;
-  const int q4 = lane >> 4, c = lane & 15;
-  const int P = p.probe_dim;
-  const bool dec = lane < G;
-  const int dq = dec ? lane : 0;
+// Online-softmax merge of an earlier state (me, le, ae) into a later one
+// (m, l, a), in the log2 domain; (-inf, 0, 0) is the identity.
+template <int PW>
+__device__ __forceinline__ void merge_into(float me, float le, const float (&ae)[PW], float& m, float& l,
+                                           float (&a)[PW]) {
+  const float M = fmaxf(me, m);
+  const float Ms = M == -INFINITY ? 0.f : M;
+  const float se = fast_exp2(me - Ms), sx = fast_exp2(m - Ms);
+  l = se * le + sx * l;
+#pragma unroll
+  for (int k = 0; k < PW; ++k) a[k] = se * ae[k] + sx * a[k];
+  m = M;
+}
 
-  float dM = -INFINITY, dL = 0.f, dn0 = 0.f;
-  float dA[PW], du[PW];
+// row_shr:K within rows of 16 lanes (the caller discards lanes whose source
+// lies outside their group).
+template <int K>
+__device__ __forceinline__ float shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + K, 0xF, 0xF, false));
+}
+
+// One inclusive-scan step over groups of CH lanes: lanes at group position
+// j >= K take the state of lane j - K as the earlier part.
+template <int K, int CH, int PW>
+__device__ __forceinline__ void scan_step(int j, float& m, float& l, float (&a)[PW]) {
+  if constexpr (K < CH) {
+    const float me = shr<K>(m), le = shr<K>(l);
+    float ae[PW];
+#pragma unroll
+    for (int k = 0; k < PW; ++k) ae[k] = shr<K>(a[k]);
+    if (j >= K) merge_into<PW>(me, le, ae, m, l, a);
+  }
+}
+
+// Probe of a state: norm n and unit direction u of the first P channels of
+// the normalised partial output (u = 0 when n = 0).
+template <int PW>
+__device__ __forceinline__ void probe_of(float L, const float (&A)[PW], float& n, float (&u)[PW]) {
+  const float rl = L > 0.f ? fast_rcp(L) : 0.f;
+  float n2 = 0.f;
 #pragma unroll
   for (int k = 0; k < PW; ++k) {
-    dA[k] = 0.f;
-    du[k] = 0.f;
+    u[k] = A[k] * rl;
+    n2 = fmaf(u[k], u[k], n2);
   }
-  int dcnt = 0, dstop = -1;
+  const float i1 = n2 > 0.f ? fast_rsq(n2) : 0.f;
+  n = n2 * i1;
+#pragma unroll
+  for (int k = 0; k < PW; ++k) u[k] *= i1;
+}
+
+// The folder wave.  It folds published block states strictly in visit order,
+// as a one-block-at-a-time streaming kernel would, but a batch at a time:
+// every consecutive position already published (up to CH = 64 / (4 GR)) is
+// taken at once.  In the scan layout lane (h, j) = h * CH + j holds head h's
+// state of the batch's block j; an inclusive scan over j (DPP row shifts)
+// gives the running state after every block of the batch, from which each
+// lane evaluates the stop rule for its position.  Consecutive-stable runs
+// come from the ballot of the per-position decisions, so one batch costs
+// about as much as one block did.  A head that stops keeps its state at its
+// stop position.  The full output (all d channels) only needs the state at
+// the end of each batch (or at the stop): every lane folds its channel slice
+// with per-block weights exp2(m_j - M), staged in LDS.
+template <typename T, int D, int GR, typename SH>
+__device__ void art_folder(const ArtArgs& p, SH& sh, int b, int g, int G, int nv) {
+  constexpr int GP = 4 * GR;
+  constexpr int CH = 64 / GP;                // batch positions per head
+  constexpr int kR = SH::kR;
+  constexpr int NBT = CH < kR ? CH : kR;     // largest batch
+  constexpr int FE = D / 16;                 // output channels per lane
+  constexpr int PW = 16;                     // probe channels held (probe_dim <= 16)
+  constexpr uint32_t RM = (CH == 32) ? 0xffffffffu : ((1u << CH) - 1u);
+  const int lane = threadIdx.x & 63;
+  const int hh = lane / CH, j = lane % CH;   // scan layout
+  const int q4 = lane >> 4, c = lane & 15;   // output layout
+  const int P = p.probe_dim;
+
+  // running state of head hh, identical in the CH lanes of its group
+  float cM = -INFINITY, cL = 0.f, cA[PW];
+#pragma unroll
+  for (int k = 0; k < PW; ++k) cA[k] = 0.f;
+  int ccnt = 0, dstop = -1;
+  bool live = hh < G;
   float A[GR][FE];
 #pragma unroll
   for (int r = 0; r < GR; ++r)
 #pragma unroll
     for (int e = 0; e < FE; ++e) A[r][e] = 0.f;
 
-  for (int t = 0; t < nb; ++t) {
-    const int s = t % kR;
-    while (ld_acq(&sh.slot_pos[s]) != t) __builtin_amdgcn_s_sleep(1);
-    // the block's slice of the full output for this lane
-    float a[GR][FE];
-#pragma unroll
-    for (int r = 0; r < GR; ++r)
-#pragma unroll
-      for (int e = 0; e < FE; ++e) a[r][e] = sh.slot_acc[s][4 * r + q4][c * FE + e];
-
-    // decision lanes: fold m, l and the probe channels, then the stop rule
-    float al = 1.f, be = 0.f;
-    int inc = 0;
-    if (dec && dstop < 0) {
-      inc = 1;
-      const float mb = sh.slot_m[s][dq], lb = sh.slot_l[s][dq];
-      const float Mn = fmaxf(dM, mb);
-      al = fast_exp2(dM - Mn);
-      be = fast_exp2(mb - Mn);
-      dL = al * dL + be * lb;
-      dM = Mn;
-      if (P > 0) {
-        const float rl = fast_rcp(dL);
-        float x[PW];
-        float n2 = 0.f;
-#pragma unroll
-        for (int k = 0; k < PW; ++k) {
-          const float ak = k < P ? sh.slot_acc[s][dq][k] : 0.f;
-          dA[k] = al * dA[k] + be * ak;
-          x[k] = dA[k] * rl;
-          n2 = fmaf(x[k], x[k], n2);
-        }
-        const float i1 = n2 > 0.f ? fast_rsq(n2) : 0.f;
-        const float n1 = n2 * i1;
-        float u2 = 0.f;
-#pragma unroll
-        for (int k = 0; k < PW; ++k) {
-          const float uk = x[k] * i1;
-          const float d = uk - du[k];
-          u2 = fmaf(d, d, u2);
-          du[k] = uk;
-        }
-        if (t >= 1) {
-          const float ds = fabsf(n1 - dn0);
-          // 1 - cos as half the squared distance of the unit vectors
-          const float dd = (n1 > 0.f && dn0 > 0.f) ? 0.5f * u2 : INFINITY;
-          const bool stable = ds < p.tau && dd < p.phi;
-          dcnt = stable ? dcnt + 1 : 0;
-          if (dcnt >= p.patience) dstop = t;
-        }
-        dn0 = n1;
-      }
+  int t0 = 0;
+  while (t0 < nv) {
+    // length of the published run of positions t0, t0 + 1, ...
+    const int tj = t0 + j;
+    const bool pub = j < NBT && tj < nv && ld_acq(&sh.slot_pos[tj % kR]) == tj;
+    const uint32_t pm = (uint32_t)__ballot(pub) & RM;  // group 0 checks every position
+    const int n = __builtin_ctz(~pm);
+    if (n == 0) {
+      __builtin_amdgcn_s_sleep(1);
+      continue;
     }
-    // every lane folds its slice of the full output with its head's factors
+    const bool in = live && j < n;
+    const int s = tj % kR;
+    float m = -INFINITY, l = 0.f, a[PW];
+#pragma unroll
+    for (int k = 0; k < PW; ++k) a[k] = 0.f;
+    if (in) {
+      m = sh.slot_m[s][hh];
+      l = sh.slot_l[s][hh];
+#pragma unroll
+      for (int k = 0; k < PW; ++k) a[k] = k < P ? sh.slot_acc[s][hh][k] : 0.f;
+    }
+    const float mb = m;
+    scan_step<1, CH, PW>(j, m, l, a);
+    scan_step<2, CH, PW>(j, m, l, a);
+    scan_step<4, CH, PW>(j, m, l, a);
+    scan_step<8, CH, PW>(j, m, l, a);
+    // state after block j = carry (+) scan_j
+    merge_into<PW>(cM, cL, cA, m, l, a);
+    float nrm, u[PW];
+    probe_of<PW>(l, a, nrm, u);
+    float cn, cu[PW];
+    probe_of<PW>(cL, cA, cn, cu);
+    float np = shr<1>(nrm), up[PW];
+#pragma unroll
+    for (int k = 0; k < PW; ++k) up[k] = shr<1>(u[k]);
+    if (j == 0) {
+      np = cn;
+#pragma unroll
+      for (int k = 0; k < PW; ++k) up[k] = cu[k];
+    }
+    float u2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < PW; ++k) {
+      const float dk = u[k] - up[k];
+      u2 = fmaf(dk, dk, u2);
+    }
+    const float ds = fabsf(nrm - np);
+    // 1 - cos as half the squared distance of the unit vectors
+    const float dd = (nrm > 0.f && np > 0.f) ? 0.5f * u2 : INFINITY;
+    const bool st = in && tj >= 1 && ds < p.tau && dd < p.phi;
+    // consecutive stable steps ending at j (plus the run carried in)
+    const uint32_t rowb = (uint32_t)(__ballot(st) >> (hh * CH)) & RM;
+    const uint32_t z = ~rowb & ((2u << j) - 1u);
+    const int run = z == 0 ? j + 1 + ccnt : j - (31 - __builtin_clz(z));
+    const bool hit = st && run >= p.patience;
+    const uint32_t rowh = (uint32_t)(__ballot(hit) >> (hh * CH)) & RM;
+    const int jend = rowh ? __builtin_ctz(rowh) : n - 1;
+    const int src = hh * CH + jend;
+    // the new running state: the state at jend
+    const float nM = __shfl(m, src), nL = __shfl(l, src);
+    const int nrun = __shfl(run, src);
+    float nA[PW];
+#pragma unroll
+    for (int k = 0; k < PW; ++k) nA[k] = k < P ? __shfl(a[k], src) : 0.f;
+    // weights of the batch's blocks in the new state, staged for the output fold
+    const float nMs = nM == -INFINITY ? 0.f : nM;
+    sh.fold_w[lane] = (in && j <= jend) ? fast_exp2(mb - nMs) : 0.f;
+    if (j == 0 && hh < GP) sh.fold_a[hh] = live ? fast_exp2(cM - nMs) : 1.f;
+    wave_lds_exchange();  // the weights are read by the other lanes
 #pragma unroll
     for (int r = 0; r < GR; ++r) {
-      float alr = 1.f, ber = 0.f;
-      int incr = 0;
+      const int hd = 4 * r + q4;
+      const float al = sh.fold_a[hd];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float aj = readlane(al, 4 * r + j), bj = readlane(be, 4 * r + j);
-        const int ij = __builtin_amdgcn_readlane(inc, 4 * r + j);
-        alr = q4 == j ? aj : alr;
-        ber = q4 == j ? bj : ber;
-        incr = q4 == j ? ij : incr;
-      }
-      if (incr) {
+      for (int e = 0; e < FE; ++e) A[r][e] *= al;
 #pragma unroll
-        for (int e = 0; e < FE; ++e) A[r][e] = alr * A[r][e] + ber * a[r][e];
+      for (int jj = 0; jj < NBT; ++jj) {
+        if (jj < n) {
+          const float w = sh.fold_w[hd * CH + jj];
+          const float* src_acc = &sh.slot_acc[(t0 + jj) % kR][hd][c * FE];
+#pragma unroll
+          for (int e = 0; e < FE; ++e) A[r][e] = fmaf(w, src_acc[e], A[r][e]);
+        }
       }
     }
-    if (lane == 0) st_rel(&sh.folded, t + 1);
-    if (__ballot(dec && dstop < 0) == 0) break;
+    wave_lds_exchange();  // before the next batch overwrites the weights
+    if (live) {
+      cM = nM;
+      cL = nL;
+#pragma unroll
+      for (int k = 0; k < PW; ++k) cA[k] = nA[k];
+      if (rowh) {
+        dstop = t0 + jend;
+        live = false;
+      } else {
+        ccnt = nrun;
+      }
+    }
+    t0 += n;
+    // once every head has stopped, the window is not advanced past this
+    // batch's start: read-ahead stays within R positions of the stop
+    if (__ballot(live) == 0) break;
+    if (lane == 0) st_rel(&sh.folded, t0);
   }
   if (lane == 0) st_rel(&sh.done, 1);
   // outputs: the frozen (or final) state of every head
 #pragma unroll
   for (int r = 0; r < GR; ++r) {
-    float Lr = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float lj = readlane(dL, 4 * r + j);
-      Lr = q4 == j ? lj : Lr;
-    }
-    const int q = 4 * r + q4;
-    if (q < G) {
-      float* dst = p.out + ((size_t)b * p.Hq + (size_t)g * G + q) * D + c * FE;
+    const int hd = 4 * r + q4;
+    const float Lr = __shfl(cL, hd * CH);
+    if (hd < G) {
+      float* dst = p.out + ((size_t)b * p.Hq + (size_t)g * G + hd) * D + c * FE;
 #pragma unroll
       for (int e = 0; e < FE; ++e) dst[e] = Lr > 0.f ? A[r][e] / Lr : 0.f;
     }
   }
-  if (dec) p.stop_pos[(size_t)b * p.Hq + (size_t)g * G + lane] = nb == 0 ? -1 : (dstop >= 0 ? dstop : nb - 1);
+  if (j == 0 && hh < G) p.stop_pos[(size_t)b * p.Hq + (size_t)g * G + hh] = dstop >= 0 ? dstop : nv - 1;
 }
 
-template <typename T, int D, int GR, int NP, int R, bool PF>
+template <typename T, int D, int GR, int NP, int R>
 __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
-  using SH = ArtShared<T, D, GR, NP, R, PF>;
+  using SH = ArtShared<T, D, GR, NP, R>;
   __shared__ SH sh;
   const int unit = blockIdx.x;
   const int b = unit / p.Hkv, g = unit % p.Hkv;
@@ -388,6 +459,8 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
   const int NBmax = p.NBmax;
   const int L = clampi(p.seq_lens ? p.seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
   const int nb = (L + kBlock - 1) / kBlock;
+  // visit positions: the whole sequence, or the first n_visit entries of the order
+  const int nv = p.n_visit ? clampi(p.n_visit[unit], 0, min(nb, p.order_stride)) : nb;
   if (threadIdx.x < R) sh.slot_pos[threadIdx.x] = -1;
   if (threadIdx.x == 0) {
     sh.folded = 0;
@@ -399,18 +472,19 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
     // the folder is the serial chain of the kernel: let the SIMD arbiter
     // prefer it over the producer waves that share its SIMD
     __builtin_amdgcn_s_setprio(3);
-    art_folder<T, D, GR, SH>(p, sh, b, g, G, nb);
+    art_folder<T, D, GR, SH>(p, sh, b, g, G, nv);
   }
   else
-    art_producer<T, D, GR, SH>(p, sh, w - 1, unit, b, g, G, L, nb);
+    art_producer<T, D, GR, SH>(p, sh, __builtin_amdgcn_readfirstlane(w - 1), unit, b, g, G, L, nb, nv);
   __syncthreads();
   if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[unit] = sh.fetched;
 }
 
 // With at least one (b, kv head) unit per CU the chip is bandwidth-bound and
-// the 8-block read-ahead keeps over-fetch small; with fewer units each
-// workgroup must pull more bandwidth by itself, so its producers pipeline
-// their loads across positions within a 16-block window.
+// an 8-block read-ahead keeps over-fetch past the stop small.  With fewer
+// units each workgroup streams at its CU's own limit and the folder, not
+// bandwidth, decides how far producers may run ahead: a 16-block window
+// lets them work on while it folds.
 template <typename T, int D>
 hipError_t launch_art_t(const ArtArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
@@ -420,12 +494,18 @@ hipError_t launch_art_t(const ArtArgs& a, hipStream_t st) {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   const dim3 grid(units);
-  if (G > 4)
-    art_kernel<T, D, 2, 7, 8, false><<<grid, 8 * 64, 0, st>>>(a);
-  else if (units >= cus)
-    art_kernel<T, D, 1, 7, 8, false><<<grid, 8 * 64, 0, st>>>(a);
-  else
-    art_kernel<T, D, 1, 7, 16, true><<<grid, 8 * 64, 0, st>>>(a);
+  const bool wide = units >= cus;
+  if (G > 4) {
+    if (wide)
+      art_kernel<T, D, 2, 7, 8><<<grid, 8 * 64, 0, st>>>(a);
+    else
+      art_kernel<T, D, 2, 7, 16><<<grid, 8 * 64, 0, st>>>(a);
+  } else {
+    if (wide)
+      art_kernel<T, D, 1, 7, 8><<<grid, 8 * 64, 0, st>>>(a);
+    else
+      art_kernel<T, D, 1, 7, 16><<<grid, 8 * 64, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

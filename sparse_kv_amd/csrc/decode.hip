@@ -184,6 +184,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
       }
       l_run[r] = l_run[r] * alpha[r] + ps;
     }
+    wave_lds_exchange();  // P rows written above are read across lanes below
 
     // rescale the running P.V sums when a query's max moved
     float al[GP];
@@ -229,6 +230,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[q][e] = fmaf(pq[q], vf[e], acc[q][e]);
     }
+    wave_lds_exchange();  // before the next block overwrites P
     if (more) load_v(jn);
   }
 

@@ -105,6 +105,16 @@ __device__ __forceinline__ float phase_sum(float x) {
   return xhalf_sum(x);
 }
 
+// Orders this wave's LDS writes before its later LDS reads of what other
+// lanes of the same wave wrote (and those reads before later overwrites).
+// One wave's LDS operations complete in order, so this only stops the
+// compiler from moving them; it emits no wait.
+__device__ __forceinline__ void wave_lds_exchange() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float readlane(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }

@@ -26,7 +26,9 @@ struct ArtArgs {
   const void* k;
   const void* v;
   const int32_t* seq_lens;
-  const int32_t* order;  // may be null
+  const int32_t* order;    // may be null: block 0, then the newest block backwards
+  int32_t order_stride;    // elements per (b, kv head) row of order
+  const int32_t* n_visit;  // may be null: visit every block of the sequence
   float tau, phi;
   int32_t patience, probe_dim;
   float* out;
@@ -49,5 +51,9 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int32_t B, 
                        int32_t NBmax, int32_t k, int32_t n_sink, int32_t n_recent,
                        int32_t max_sel, int32_t* idx, int32_t* n_sel, hipStream_t st);
 hipError_t launch_art(const ArtArgs& a, hipStream_t st);
+// Largest number of non-sink blocks a sequence may have for launch_order.
+constexpr int32_t kOrderMaxRest = 16384;
+hipError_t launch_order(const float* scores, const int32_t* seq_lens, int32_t B, int32_t Hkv,
+                        int32_t NBmax, int32_t* order, hipStream_t st);
 
 }  // namespace skv

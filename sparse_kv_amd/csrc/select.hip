@@ -222,6 +222,45 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   if (tid == 0) n_sel[unit] = min(total, max_sel);
 }
 
+// ---- importance order: one workgroup per (b, kv head) -------------------
+// Block 0 first, then blocks 1 .. nb-1 by descending score, lower index first
+// among equal scores ("ART" summary, §2.4, importance-first visit order).
+// The nb - 1 keys (inverted score key << 32 | block) are sorted ascending by
+// a bitonic network in LDS, padded to a power of two with all-ones keys.
+template <int CAP>
+__global__ __launch_bounds__(1024) void order_kernel(const float* __restrict__ scores,
+                                                     const int32_t* __restrict__ seq_lens, int32_t Hkv,
+                                                     int32_t NBmax, int32_t* __restrict__ order) {
+  __shared__ uint64_t key[CAP];
+  const int unit = blockIdx.x, b = unit / Hkv, tid = threadIdx.x;
+  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
+  const int nb = (L + kBlock - 1) / kBlock;
+  const float* row = scores + (size_t)unit * NBmax;
+  int32_t* out = order + (size_t)unit * NBmax;
+  const int nr = max(nb - 1, 0);  // blocks after the sink
+  int n = 2;
+  while (n < nr) n <<= 1;
+  for (int i = tid; i < n; i += 1024)
+    key[i] = i < nr ? ((uint64_t)~score_key(row[i + 1]) << 32) | (uint32_t)(i + 1) : ~(uint64_t)0;
+  __syncthreads();
+  for (int kk = 2; kk <= n; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int pr = tid; pr < (n >> 1); pr += 1024) {
+        const int i = 2 * j * (pr / j) + pr % j;  // pair (i, i + j)
+        const uint64_t x = key[i], y = key[i + j];
+        const bool up = (i & kk) == 0;
+        if ((x > y) == up) {
+          key[i] = y;
+          key[i + j] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < NBmax; i += 1024)
+    out[i] = i == 0 ? (nb > 0 ? 0 : -1) : (i < nb ? (int32_t)(uint32_t)key[i - 1] : -1);
+}
+
 }  // namespace
 
 hipError_t launch_build_centroids(const void* k, const int32_t* seq_lens, float* c, int32_t B,
@@ -268,6 +307,17 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int32_t B, 
   if (B == 0) return hipSuccess;
   topk_kernel<<<dim3(B * Hkv), 256, 0, st>>>(scores, seq_lens, Hkv, NBmax, k, n_sink, n_recent,
                                              max_sel, idx, n_sel);
+  return hipGetLastError();
+}
+
+hipError_t launch_order(const float* scores, const int32_t* seq_lens, int32_t B, int32_t Hkv,
+                        int32_t NBmax, int32_t* order, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  if (NBmax - 1 > kOrderMaxRest) return hipErrorInvalidValue;
+  if (NBmax - 1 <= 4096)
+    order_kernel<4096><<<dim3(B * Hkv), 1024, 0, st>>>(scores, seq_lens, Hkv, NBmax, order);
+  else
+    order_kernel<kOrderMaxRest><<<dim3(B * Hkv), 1024, 0, st>>>(scores, seq_lens, Hkv, NBmax, order);
   return hipGetLastError();
 }
 

@@ -86,6 +86,21 @@ def test_argument_validation(skv):
     assert lib.attn_decode_art(ctypes.byref(d), *args, 1e-3, 1e-4, 2, 17, FAKE, FAKE, None, None) == -2
     assert lib.attn_decode_art(ctypes.byref(d), *args, float("nan"), 1e-4, 2, 8, FAKE, FAKE, None, None) == -1
     assert lib.attn_decode_art(ctypes.byref(d), *args, 1e-3, 1e-4, 2, 8, None, FAKE, None, None) == -1
+    # ART over a list: the list, its counts and max_list >= 1 are required
+    lst = [FAKE, FAKE, FAKE, None]
+    assert lib.attn_decode_art_list(ctypes.byref(d), *lst, None, FAKE, 4, 1e-3, 1e-4, 2, 8, FAKE, FAKE, None,
+                                    None) == -1
+    assert lib.attn_decode_art_list(ctypes.byref(d), *lst, FAKE, None, 4, 1e-3, 1e-4, 2, 8, FAKE, FAKE, None,
+                                    None) == -1
+    assert lib.attn_decode_art_list(ctypes.byref(d), *lst, FAKE, FAKE, 0, 1e-3, 1e-4, 2, 8, FAKE, FAKE, None,
+                                    None) == -1
+    assert lib.attn_decode_art_list(ctypes.byref(d), *lst, FAKE, FAKE, 4, 1e-3, 1e-4, 0, 8, FAKE, FAKE, None,
+                                    None) == -1
+    # importance order: scores and order are required; at most 16384 blocks after the sink
+    assert lib.attn_order_blocks(ctypes.byref(d), None, None, FAKE, None) == -1
+    assert lib.attn_order_blocks(ctypes.byref(d), FAKE, None, None, None) == -1
+    assert lib.attn_order_blocks(ctypes.byref(dims(max_blocks=16386)), FAKE, None, FAKE, None) == -2
+    assert lib.attn_order_blocks(ctypes.byref(dims(batch=0, max_blocks=16385)), FAKE, None, FAKE, None) == 0
     # empty batch is a no-op success
     d0 = dims(batch=0)
     assert lib.attn_decode_dense(ctypes.byref(d0), FAKE, FAKE, FAKE, None, 0, -1, 4, FAKE, FAKE, FAKE, None) == 0

@@ -152,3 +152,58 @@ def test_routed_36_layer_stack_256k():
                          f"layer {i} ({'FA' if mask[i] else 'SA'}) kv head {g}")
     for o in outs:
         assert torch.isfinite(o).all()
+
+
+def test_importance_first_art_128k_batch8():
+    """Centroid scores -> importance order -> ART at 128K batch 8 (mixture keys).
+
+    The order kernel's result is checked as a descending sort of the oracle's
+    float64 scores; stop positions and outputs are checked exactly with the
+    oracle's own order placed in the sampled rows."""
+    W3, W4 = synth.WORKLOADS[3], synth.WORKLOADS[4]
+    B, Hq, Hkv, d, L = W3["B"], W3["Hq"], W3["Hkv"], W3["d"], W3["L"]
+    tau, phi, p, probe = W4["tau"], W4["phi"], W4["patience"], W4["probe_dim"]
+    nb = L // 64
+    t = time.time()
+    inp = synth.make_inputs(3, B, Hq, Hkv, d, L, kind="mixture")
+    log(f"[full] importance-first ART 128K batch 8: inputs in {time.time() - t:.1f}s")
+    import sparse_kv_amd as skv
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    order = skv.attn_order_blocks(skv.attn_score_centroids(q, skv.attn_build_centroids(k)))
+    out, stop, fetched = skv.attn_decode_art(q, k, v, None, order=order, tau=tau, phi=phi, patience=p,
+                                             probe_dim=probe)
+    torch.cuda.synchronize()
+    order_h = order.cpu().numpy()
+    log(f"  GPU chain: mean stop {stop.float().mean().item():.1f}, mean blocks fetched "
+        f"{fetched.float().mean().item():.1f} of {nb}")
+    G = Hq // Hkv
+    # every ART decision of a checked unit must clear a 1% band around the
+    # thresholds; scan units in a fixed order until three do
+    units = SAMPLE + [(b, g) for b in range(B) for g in range(Hkv) if (b, g) not in SAMPLE]
+    oracle_rows, ref = {}, {}
+    for i, (b, g) in enumerate(units):
+        qf, kf, vf, seq = unit_f64(inp, b, g)
+        sc = oracle.centroid_scores(qf, oracle.block_centroids(kf, seq), seq, inp.scale)[0, 0]
+        o = order_h[b, g]
+        assert o[0] == 0 and sorted(o.tolist()) == list(range(nb)), f"unit ({b},{g}) order is no permutation"
+        assert np.min(sc[o[1:-1]] - sc[o[2:]]) > -1e-4, f"unit ({b},{g}) order is not descending"
+        oo = oracle.importance_order(sc.astype(np.float32), nb)
+        ro, rs, tr = oracle.art_decode(qf, kf, vf, seq, inp.scale, tau, phi, p, probe, order=[[oo]])
+        if all(art_margin_ok(x, tau, phi) for x in tr.values()):
+            oracle_rows[(b, g)] = oo
+            ref[(b, g)] = (ro[0], rs[0])
+            if len(ref) == 3:
+                break
+    log(f"  {len(ref)} of {i + 1} scanned units clear the ART decision margins")
+    assert len(ref) >= 2
+    inj = order_h.copy()
+    for (b, g), oo in oracle_rows.items():
+        inj[b, g] = oo
+    out2, stop2, _ = skv.attn_decode_art(q, k, v, None, order=torch.from_numpy(inj).cuda(), tau=tau, phi=phi,
+                                         patience=p, probe_dim=probe)
+    torch.cuda.synchronize()
+    out2, stop2 = out2.cpu().numpy(), stop2.cpu().numpy()
+    for (b, g), (ro, rs) in ref.items():
+        assert stop2[b, g * G:(g + 1) * G].tolist() == rs.tolist(), f"stop positions of unit ({b},{g})"
+        assert_close(out2[b, g * G:(g + 1) * G], ro, TOL, f"importance-first ART unit ({b},{g})")
