@@ -24,10 +24,24 @@ top-k comparison on the scores rounded to float32, the precision the
 kernels decide in.  On inputs whose k-th / (k+1)-th gap exceeds 1e-4 the two
 are the same decision.
 
+* Two levels (Squeezed Attention blog, Q2 step 4, optional hierarchical
+  clustering; Q1 on hierarchical clustering): coarse groups are searched
+  first, then the fine groups inside the relevant coarse ones.  Reading: a
+  coarse group is `group` consecutive blocks (a super-block) whose centroid
+  is the mean of its valid keys; the coarse score is the same scaled dot
+  product; the k_coarse best super-blocks that hold at least one non-forced
+  block are kept (ties to the lower index), and the k fine picks are made
+  among the non-forced blocks inside them.  Forced blocks are added as in the
+  one-level choice.
+
 Pins: tests/test_oracle_selection.py (the centroid/score identity against a
 per-token pure-Python brute force, a brute-force sort, k >= |candidates|
 selecting everything, constructed ties, and the Squeezed Attention worked
-example of six keys in two clusters, tests/golden/squeezed_toy.json).
+example of six keys in two clusters, tests/golden/squeezed_toy.json; for
+two levels: super-block centroids against a per-token brute-force mean,
+k_coarse covering every super-block and group = 1 both reducing to the
+one-level choice, and a constructed case where the coarse level hides a
+block the one-level choice would take).
 The split of k versus forced blocks is a reading: parity unpinned beyond the
 brute-force sort.
 """
@@ -119,3 +133,74 @@ def selection_gap(scores_row, nb: int, k: int, n_sink: int, n_recent: int):
         return math.inf
     s = np.sort(np.asarray(scores_row, dtype=np.float64)[cand])[::-1]
     return float(s[k - 1] - s[k])
+
+
+def super_centroids(k, seq_lens, group: int, block: int = 64):
+    """Mean key of every super-block of `group` consecutive blocks:
+    C2 [B, Hkv, ceil(NBmax / group), d]; zeros past the sequence's end."""
+    B, Hkv, Lmax, d = k.shape
+    span = group * block
+    NS = -(-num_blocks(Lmax, block) // group)
+    C = np.zeros((B, Hkv, NS, d))
+    for b in range(B):
+        L = int(seq_lens[b])
+        for s_ in range(-(-L // span)):
+            lo, hi = s_ * span, min((s_ + 1) * span, L)
+            C[b, :, s_] = k[b, :, lo:hi].mean(axis=1)
+    return C
+
+
+def select_blocks_two_level(fine_row, coarse_row, nb: int, group: int, k_coarse: int, k: int,
+                            n_sink: int, n_recent: int):
+    """Two-level selection for one KV head (ascending block list).
+
+    The super-blocks holding a non-forced block compete on their float32
+    coarse score (lower index first among equals); the k_coarse best are
+    opened and min(k, |their non-forced blocks|) blocks are picked among
+    those on the float32 fine score (lower index first); forced blocks are
+    added.
+    """
+    F = forced_blocks(nb, n_sink, n_recent)
+    ns = -(-nb // group)
+    members = {s_: [j for j in range(s_ * group, min((s_ + 1) * group, nb)) if j not in F] for s_ in range(ns)}
+    eligible = [s_ for s_ in range(ns) if members[s_]]
+    c32 = np.asarray(coarse_row, dtype=np.float64).astype(np.float32)
+    opened = sorted(eligible, key=lambda s_: (-float(c32[s_]), s_))[:max(k_coarse, 0)]
+    cand = sorted(j for s_ in opened for j in members[s_])
+    f32 = np.asarray(fine_row, dtype=np.float64).astype(np.float32)
+    picks = sorted(cand, key=lambda j: (-float(f32[j]), j))[:max(k, 0)]
+    return sorted(F | set(picks))
+
+
+def select_all_two_level(fine, coarse, seq_lens, group: int, k_coarse: int, k: int, n_sink: int,
+                         n_recent: int, block: int = 64):
+    """select_blocks_two_level for every (b, g): nested lists [B][Hkv]."""
+    B, Hkv, _ = fine.shape
+    out = []
+    for b in range(B):
+        nb = num_blocks(int(seq_lens[b]), block)
+        out.append([select_blocks_two_level(fine[b, g], coarse[b, g], nb, group, k_coarse, k, n_sink, n_recent)
+                    for g in range(Hkv)])
+    return out
+
+
+def two_level_gaps(fine_row, coarse_row, nb: int, group: int, k_coarse: int, k: int, n_sink: int,
+                   n_recent: int):
+    """(coarse gap, fine gap): the score gaps at the two decision boundaries
+    (inf where there is no boundary), for certifying margins in tests."""
+    F = forced_blocks(nb, n_sink, n_recent)
+    ns = -(-nb // group)
+    members = {s_: [j for j in range(s_ * group, min((s_ + 1) * group, nb)) if j not in F] for s_ in range(ns)}
+    eligible = [s_ for s_ in range(ns) if members[s_]]
+    cg = math.inf
+    if 0 < k_coarse < len(eligible):
+        cs = np.sort(np.asarray(coarse_row, dtype=np.float64)[eligible])[::-1]
+        cg = float(cs[k_coarse - 1] - cs[k_coarse])
+    c64 = np.asarray(coarse_row, dtype=np.float64)
+    opened = sorted(eligible, key=lambda s_: (-c64[s_], s_))[:max(k_coarse, 0)]
+    cand = [j for s_ in opened for j in members[s_]]
+    fg = math.inf
+    if 0 < k < len(cand):
+        fs = np.sort(np.asarray(fine_row, dtype=np.float64)[cand])[::-1]
+        fg = float(fs[k - 1] - fs[k])
+    return cg, fg

@@ -115,3 +115,75 @@ def test_squeezed_worked_example():
     assert np.max(np.abs(out[0, 0] - np.array(ref))) < 1e-14
     # and it differs from full attention (the other cluster is really dropped)
     assert np.max(np.abs(out - oracle.decode_dense(q, K, V, seq, scale, block=bs))) > 1e-3
+
+
+# ---- two-level (super-block) selection -------------------------------------
+
+from oracle.selection import select_blocks_two_level, super_centroids, two_level_gaps  # noqa: E402
+
+
+def test_super_centroids_are_means_of_their_tokens():
+    r = np.random.default_rng(11)
+    k = r.standard_normal((2, 1, 30, 4))
+    seq = np.array([30, 13])
+    C2 = super_centroids(k, seq, group=2, block=4)  # super-blocks of 8 tokens
+    assert C2.shape == (2, 1, 4, 4)
+    for b in range(2):
+        L = int(seq[b])
+        for s_ in range(4):
+            toks = list(range(8 * s_, min(8 * s_ + 8, L)))
+            if toks:
+                ref = brute.mean_rows([list(k[b, 0, t]) for t in toks])
+                assert np.max(np.abs(C2[b, 0, s_] - np.array(ref))) < 1e-15
+            else:
+                assert not C2[b, 0, s_].any()
+    # the coarse score is the mean logit of the super-block's tokens (linearity)
+    q = r.standard_normal((2, 2, 4))
+    sig2 = centroid_scores(q, C2, np.array([4, 2]), 0.7, block=1)  # lengths in super-blocks
+    for b in range(2):
+        L = int(seq[b])
+        qsum = [q[b, 0, i] + q[b, 1, i] for i in range(4)]
+        for s_ in range(-(-L // 8)):
+            toks = range(8 * s_, min(8 * s_ + 8, L))
+            ref = sum(0.7 * brute.dot(qsum, list(k[b, 0, t])) for t in toks) / len(toks)
+            assert abs(sig2[b, 0, s_] - ref) < 1e-13
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_two_level_reduces_to_one_level(seed):
+    r = np.random.default_rng(100 + seed)
+    nb = int(r.integers(1, 70))
+    group = int(r.integers(1, 9))
+    fine = r.standard_normal(nb)
+    coarse = r.standard_normal(-(-nb // group))
+    k = int(r.integers(0, nb + 2))
+    ns, nr = int(r.integers(0, 3)), int(r.integers(0, 8))
+    # every super-block opened: the one-level choice
+    assert select_blocks_two_level(fine, coarse, nb, group, 10 ** 6, k, ns, nr) == select_blocks(fine, nb, k, ns, nr)
+    # group = 1 with coarse = fine: the one-level choice with min(k, k_coarse) picks
+    kc = int(r.integers(0, nb + 2))
+    assert select_blocks_two_level(fine, fine, nb, 1, kc, k, ns, nr) == select_blocks(fine, nb, min(k, kc), ns, nr)
+
+
+def test_two_level_coarse_gate():
+    # 3 super-blocks of 4 blocks.  Super-block 1 has the best mean, super-block
+    # 2 holds the single best block.  One-level top-2 takes block 9 (in super-
+    # block 2); two-level with one opened super-block stays inside super-block 1.
+    fine = np.array([0.0, 0.1, 0.2, 0.3, 2.0, 2.5, 2.2, 2.1, -1.0, 9.0, -1.0, -1.0])
+    coarse = np.array([0.15, 2.2, 1.5])
+    assert select_blocks(fine, 12, 2, 0, 0) == [5, 9]
+    assert select_blocks_two_level(fine, coarse, 12, 4, 1, 2, 0, 0) == [5, 6]
+    assert select_blocks_two_level(fine, coarse, 12, 4, 2, 2, 0, 0) == [5, 9]
+    # forced sink and window: super-block 0 keeps candidates 1-3, super-block 2
+    # none once the window covers blocks 8-11, so it cannot be opened
+    assert select_blocks_two_level(fine, coarse, 12, 4, 1, 2, 1, 4) == [0, 5, 6, 8, 9, 10, 11]
+    assert select_blocks_two_level(fine, coarse, 12, 4, 2, 5, 1, 4) == [0, 3, 4, 5, 6, 7, 8, 9, 10, 11]
+    # ties: the lower super-block and the lower block win
+    assert select_blocks_two_level(np.ones(8), np.ones(2), 8, 4, 1, 2, 0, 0) == [0, 1]
+    # k_coarse = 0 or k = 0 keep only forced blocks; an empty sequence selects nothing
+    assert select_blocks_two_level(fine, coarse, 12, 4, 0, 5, 1, 1) == [0, 11]
+    assert select_blocks_two_level(fine, coarse, 12, 4, 3, 0, 1, 1) == [0, 11]
+    assert select_blocks_two_level(fine, coarse, 0, 4, 3, 3, 1, 1) == []
+    # the gap helper sees both boundaries
+    cg, fg = two_level_gaps(fine, coarse, 12, 4, 1, 2, 0, 0)
+    assert abs(cg - 0.7) < 1e-12 and abs(fg - 0.3) < 1e-12
