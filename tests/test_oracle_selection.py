@@ -186,4 +186,4 @@ def test_two_level_coarse_gate():
     assert select_blocks_two_level(fine, coarse, 0, 4, 3, 3, 1, 1) == []
     # the gap helper sees both boundaries
     cg, fg = two_level_gaps(fine, coarse, 12, 4, 1, 2, 0, 0)
-    assert abs(cg - 0.7) < 1e-12 and abs(fg - 0.3) < 1e-12
+    assert abs(cg - 0.7) < 1e-12 and abs(fg - 0.1) < 1e-12
