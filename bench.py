@@ -11,7 +11,9 @@ One timed step runs every stage of the hot path over that batch:
   art     ART early-terminated decode, block 0 then most recent first
   window  sink + recent-window decode + merge                 (routed SA layer)
 Optional (--stages ...,art_imp): centroid scores + importance order + ART
-visiting block 0 then blocks by descending centroid score.
+visiting block 0 then blocks by descending centroid score.  Optional
+(--stages ...,sparse2): two-level selection (super-blocks of 16 blocks, 32
+opened, then the same 205 picks + sink + window) + listed-block decode + merge.
 Block centroids are built once before timing (they change only when a block
 fills).  Each stage reads its own copy of the KV cache so that no stage is
 served from the 256 MB last-level cache filled by the previous one.
@@ -72,7 +74,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", default="dense,sparse,art,window",
-                    help="comma list of dense, sparse, art, window, art_imp")
+                    help="comma list of dense, sparse, art, window, art_imp, sparse2")
     ap.add_argument("--splits-per-shard", type=int, default=4, help="hybrid256k: inner splits per context shard")
     ap.add_argument("--sa-splits", type=int, default=32, help="hybrid256k: splits of a sink+window layer")
     ap.add_argument("--workload", default="decode128k", choices=["decode128k", "art64k", "hybrid256k"],
@@ -120,7 +122,7 @@ def main():
     q = up(inp.q)
     copies = {}
     k0, v0 = up(inp.k), up(inp.v)
-    for i, s in enumerate(("dense", "sparse", "art", "window", "art_imp")):
+    for i, s in enumerate(("dense", "sparse", "art", "window", "art_imp", "sparse2")):
         if s in stages or s == "dense":
             copies[s] = (k0, v0) if i == 0 else (k0.clone(), v0.clone())
     torch.cuda.synchronize()
@@ -131,6 +133,9 @@ def main():
     C = skv.attn_build_centroids(copies["sparse"][0]) if "sparse" in stages else None
     c_ev[1].record()
     C_imp = skv.attn_build_centroids(copies["art_imp"][0]) if "art_imp" in stages else None
+    group2, kc2 = 16, 32
+    C_2 = skv.attn_build_centroids(copies["sparse2"][0]) if "sparse2" in stages else None
+    C2_2 = skv.attn_build_super_centroids(C_2, group2) if "sparse2" in stages else None
     win_idx, win_n = skv.attn_select_topk(None, None, k=0, n_sink_blocks=n_sink, n_recent_blocks=win_recent,
                                           shape=(B, Hkv, NB), device=dev)
     torch.cuda.synchronize()
@@ -149,6 +154,10 @@ def main():
     stop = torch.empty((B, Hq), dtype=torch.int32, device=dev)
     fetched = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
     scores_i = torch.empty((B, Hkv, NB), **f32)
+    sel2_idx = torch.empty((B, Hkv, max_sel), dtype=torch.int32, device=dev)
+    sel2_n = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    st_2 = (torch.empty((B, Hq, Ss), **f32), torch.empty((B, Hq, Ss), **f32), torch.empty((B, Hq, Ss, d), **f32))
+    out_2 = torch.empty((B, Hq, d), **f32)
     order_i = torch.empty((B, Hkv, NB), dtype=torch.int32, device=dev)
     out_i = torch.empty((B, Hq, d), **f32)
     stop_i = torch.empty((B, Hq), dtype=torch.int32, device=dev)
@@ -192,6 +201,15 @@ def main():
             skv.attn_decode_sparse(q, kw, vw, win_idx, win_n, None, num_splits=Sw, m=st_w[0], l=st_w[1], o=st_w[2])
             skv.attn_merge_states(*st_w, out=out_w)
             mark("window.1")
+        if "sparse2" in stages:
+            k2, v2 = copies["sparse2"]
+            mark("sparse2.0")
+            skv.attn_select_two_level(q, C_2, C2_2, group2, None, k_coarse=kc2, k=topk, n_sink_blocks=n_sink,
+                                      n_recent_blocks=n_recent, max_sel=max_sel, block_idx=sel2_idx, n_sel=sel2_n)
+            mark("sparse2.sel")
+            skv.attn_decode_sparse(q, k2, v2, sel2_idx, sel2_n, None, num_splits=Ss, m=st_2[0], l=st_2[1], o=st_2[2])
+            skv.attn_merge_states(*st_2, out=out_2)
+            mark("sparse2.1")
         if "art_imp" in stages:
             ki, vi = copies["art_imp"]
             mark("art_imp.0")
@@ -255,6 +273,19 @@ def main():
         by = float(win_n.cpu().numpy().sum()) * kv_block + q_bytes + o_bytes
         total_bytes += by
         paths["window"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), tokens_per_s=B / (ms * 1e-3), splits=Sw)
+    if "sparse2" in stages:
+        n2 = sel2_n.cpu().numpy()
+        ms = avg_ms("sparse2.0", "sparse2.1")
+        NS2 = -(-NB // group2)
+        by = (float(n2.sum()) * kv_block + units * NS2 * d * 4 + units * kc2 * group2 * d * 4 + q_bytes + o_bytes)
+        total_bytes += by
+        paths["sparse2"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), select_ms=avg_ms("sparse2.0", "sparse2.sel"),
+                                blocks_per_unit=float(n2.mean()), group=group2, opened=kc2,
+                                tokens_per_s=B / (ms * 1e-3), splits=Ss)
+        if "dense" in stages:
+            paths["sparse2"]["max_abs_err_vs_dense"] = float((out_2.double() - out_d.double()).abs().max())
+            if "sparse" in stages:
+                paths["sparse"]["max_abs_err_vs_dense"] = float((out_s.double() - out_d.double()).abs().max())
     if "art_imp" in stages:
         stp = stop_i.cpu().numpy().reshape(B, Hkv, Hq // Hkv)
         need = stp.max(axis=2) + 1
@@ -275,7 +306,7 @@ def main():
             if "art" in stages:
                 paths["art"]["max_abs_err_vs_dense"] = float((out_a.double() - ref).abs().max())
     if "dense" in paths:
-        for k_ in ("sparse", "art", "window", "art_imp"):
+        for k_ in ("sparse", "art", "window", "art_imp", "sparse2"):
             if k_ in paths:
                 paths[k_]["speedup_vs_dense"] = paths["dense"]["ms"] / paths[k_]["ms"]
 

@@ -110,6 +110,24 @@ int attn_build_centroids(const attn_dims* dims, const void* k, const int32_t* se
                          float* centroids, void* stream);
 
 /*
+ * Incremental centroid refresh after tokens were appended to the cache.
+ * Defines: "Squeezed Attention" blog, Q2 step 1 (the centroids stand for the
+ * current keys) -- after the call, centroids equal what attn_build_centroids
+ * would write for seq_lens, for every block of the refreshed range.
+ *   prev_lens  int32 [B] or NULL: each row's length when its centroids were
+ *              last built.  Refreshed blocks: [min(prev_len, L) / 64,
+ *              max(nb, the previous block count)) -- the block that held the
+ *              shorter end onwards; blocks past the new end are zeroed.  NULL refreshes
+ *              only the last block of each row (one token appended).  Blocks
+ *              outside the range are neither read nor written.
+ *   span_hint  >= 1: expected blocks per row, sizes the launch (any span is
+ *              handled; a small hint only means fewer waves per row).
+ *   centroids  float [B, Hkv, max_blocks, d], updated in place.
+ */
+int attn_update_centroids(const attn_dims* dims, const void* k, const int32_t* seq_lens,
+                          const int32_t* prev_lens, int32_t span_hint, float* centroids, void* stream);
+
+/*
  * Query-versus-centroid block scores, one per KV head.
  * Defines: "Squeezed Attention" blog, Q1 and Q2 step 2 (compare the query
  * with the centroids to decide which keys to load); one score per GQA group
@@ -139,6 +157,44 @@ int attn_score_centroids(const attn_dims* dims, const void* q, const float* cent
 int attn_select_topk(const attn_dims* dims, const float* scores, const int32_t* seq_lens,
                      int32_t k, int32_t n_sink_blocks, int32_t n_recent_blocks, int32_t max_sel,
                      int32_t* block_idx, int32_t* n_sel, void* stream);
+
+/*
+ * Super-block centroids for two-level selection.
+ * Defines: "Squeezed Attention" blog, Q2 step 4 (optional hierarchical
+ * clustering: a coarse level of groups above the fine one) -- here a coarse
+ * group is `group` consecutive blocks and its centroid the mean of its valid
+ * keys, computed from the block centroids weighted by their token counts.
+ *   centroids        float [B, Hkv, max_blocks, d] (attn_build_centroids).
+ *   super_centroids  float [B, Hkv, ceil(max_blocks / group), d] out; super-
+ *                    blocks past the sequence's end are zeros.
+ * Requires group >= 1.
+ */
+int attn_build_super_centroids(const attn_dims* dims, const float* centroids, const int32_t* seq_lens,
+                               int32_t group, float* super_centroids, void* stream);
+
+/*
+ * Two-level block selection.
+ * Defines: "Squeezed Attention" blog, Q2 step 4 and Q1 (search the coarse
+ * groups first, then the fine groups inside the relevant ones; the search
+ * cost falls from linear towards logarithmic in the context length), with
+ * the one-level rules of attn_select_topk: forced sink [0, n_sink) and
+ * window [nb - n_recent, nb) blocks, scores sigma = scale * <sum of the GQA
+ * group's queries, centroid>, float32 ranking with the lower index first
+ * among equal scores.  Per (b, g): the super-blocks holding a non-forced
+ * block are ranked on their coarse score and the best k_coarse opened; the
+ * non-forced blocks inside them are ranked on their fine score and the best
+ * k taken.  Only the opened super-blocks' fine centroids are read.
+ *   q                [B, Hq, d] (the scoring query; any query-shaped vector).
+ *   block_idx, n_sel as attn_select_topk (ascending, -1 padded).
+ * Requires group >= 1, k_coarse >= 0, k >= 0, max_sel >= min(n_sink +
+ * n_recent + k, max_blocks); ceil(max_blocks / group) <= 4096 and
+ * min(k_coarse, ceil(max_blocks / group)) * group <= 8192 (else
+ * ATTN_ERR_UNSUPPORTED).
+ */
+int attn_select_two_level(const attn_dims* dims, const void* q, const float* centroids,
+                          const float* super_centroids, const int32_t* seq_lens, int32_t group,
+                          int32_t k_coarse, int32_t k, int32_t n_sink_blocks, int32_t n_recent_blocks,
+                          int32_t max_sel, int32_t* block_idx, int32_t* n_sel, void* stream);
 
 /*
  * Split-KV decode attention restricted to listed blocks.

@@ -28,8 +28,11 @@ EXPORTS = (
     "attn_decode_dense",
     "attn_merge_states",
     "attn_build_centroids",
+    "attn_update_centroids",
     "attn_score_centroids",
     "attn_select_topk",
+    "attn_build_super_centroids",
+    "attn_select_two_level",
     "attn_decode_sparse",
     "attn_decode_art",
     "attn_decode_art_list",
@@ -61,8 +64,11 @@ _SIG = {
     "attn_decode_dense": [_D, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
     "attn_merge_states": [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P],
     "attn_build_centroids": [_D, _P, _P, _P, _P],
+    "attn_update_centroids": [_D, _P, _P, _P, _I, _P, _P],
     "attn_score_centroids": [_D, _P, _P, _P, _P, _P],
     "attn_select_topk": [_D, _P, _P, _I, _I, _I, _I, _P, _P, _P],
+    "attn_build_super_centroids": [_D, _P, _P, _I, _P, _P],
+    "attn_select_two_level": [_D, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P],
     "attn_decode_sparse": [_D, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P],
     "attn_decode_art": [_D, _P, _P, _P, _P, _P, _F, _F, _I, _I, _P, _P, _P, _P],
     "attn_decode_art_list": [_D, _P, _P, _P, _P, _P, _P, _I, _F, _F, _I, _I, _P, _P, _P, _P],
@@ -255,6 +261,24 @@ def attn_build_centroids(k, seq_lens=None, out=None, num_q_heads=None):
     return out
 
 
+def attn_update_centroids(k, centroids, seq_lens=None, prev_lens=None, span_hint=1):
+    """Refresh centroids [B, Hkv, NBmax, d] in place after tokens were appended (see the C header)."""
+    dev = k.device
+    _need(k, "k", dev)
+    B, Hkv, Lmax, d = k.shape
+    if Lmax % BLOCK:
+        raise ValueError(f"KV length {Lmax} must be a multiple of {BLOCK}")
+    _need(centroids, "centroids", dev, torch.float32, (B, Hkv, Lmax // BLOCK, d))
+    dims = AttnDims(B, Hkv, Hkv, d, BLOCK, Lmax // BLOCK, _dtype_code(k), 1.0)
+    seq = _seq(seq_lens, B, dev)
+    prev = None if prev_lens is None else _need(prev_lens, "prev_lens", dev, torch.int32, (B,))
+    with _on_device(dev):
+        st = lib().attn_update_centroids(ctypes.byref(dims), _ptr(k), _ptr(seq), _ptr(prev), int(span_hint),
+                                        _ptr(centroids), _stream(dev))
+    _check(st, "attn_update_centroids")
+    return centroids
+
+
 def attn_score_centroids(q, centroids, seq_lens=None, scale=None, out=None):
     """Group scores [B, Hkv, NBmax] float32 (-inf past each sequence's end)."""
     dev = q.device
@@ -301,6 +325,54 @@ def attn_select_topk(scores, seq_lens=None, k=0, n_sink_blocks=1, n_recent_block
                                    int(n_recent_blocks), int(max_sel), _ptr(block_idx), _ptr(n_sel),
                                    _stream(dev))
     _check(st, "attn_select_topk")
+    return block_idx, n_sel
+
+
+def attn_build_super_centroids(centroids, group, seq_lens=None, out=None):
+    """Super-block centroids [B, Hkv, ceil(NBmax / group), d] from block centroids."""
+    dev = centroids.device
+    _need(centroids, "centroids", dev, torch.float32)
+    if centroids.dim() != 4:
+        raise ValueError("centroids must be [B, Hkv, NBmax, d]")
+    B, Hkv, NBmax, d = centroids.shape
+    group = int(group)
+    if group < 1:
+        raise ValueError("group must be >= 1")
+    dims = AttnDims(B, Hkv, Hkv, d, BLOCK, NBmax, ATTN_F32, 1.0)
+    seq = _seq(seq_lens, B, dev)
+    out = _out(out, (B, Hkv, -(-NBmax // group), d), torch.float32, dev, "out")
+    with _on_device(dev):
+        st = lib().attn_build_super_centroids(ctypes.byref(dims), _ptr(centroids), _ptr(seq), group, _ptr(out),
+                                             _stream(dev))
+    _check(st, "attn_build_super_centroids")
+    return out
+
+
+def attn_select_two_level(q, centroids, super_centroids, group, seq_lens=None, k_coarse=16, k=0,
+                          n_sink_blocks=1, n_recent_blocks=0, max_sel=None, scale=None, block_idx=None,
+                          n_sel=None):
+    """Two-level selection: (block_idx [B, Hkv, max_sel] ascending, -1 padded; n_sel [B, Hkv])."""
+    dev = q.device
+    _need(q, "q", dev)
+    _need(centroids, "centroids", dev, torch.float32)
+    B, Hq, d = q.shape
+    Bc, Hkv, NBmax, dc = centroids.shape
+    if Bc != B or dc != d:
+        raise ValueError("q and centroids disagree")
+    _need(super_centroids, "super_centroids", dev, torch.float32, (B, Hkv, -(-NBmax // int(group)), d))
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if max_sel is None:
+        max_sel = max(1, min(NBmax, int(n_sink_blocks) + int(n_recent_blocks) + int(k)))
+    dims = AttnDims(B, Hq, Hkv, d, BLOCK, NBmax, _dtype_code(q), s)
+    seq = _seq(seq_lens, B, dev)
+    block_idx = _out(block_idx, (B, Hkv, max_sel), torch.int32, dev, "block_idx")
+    n_sel = _out(n_sel, (B, Hkv), torch.int32, dev, "n_sel")
+    with _on_device(dev):
+        st = lib().attn_select_two_level(ctypes.byref(dims), _ptr(q), _ptr(centroids), _ptr(super_centroids),
+                                        _ptr(seq), int(group), int(k_coarse), int(k), int(n_sink_blocks),
+                                        int(n_recent_blocks), int(max_sel), _ptr(block_idx), _ptr(n_sel),
+                                        _stream(dev))
+    _check(st, "attn_select_two_level")
     return block_idx, n_sel
 
 

@@ -140,6 +140,17 @@ int attn_build_centroids(const attn_dims* dims, const void* k, const int32_t* se
                                                 (hipStream_t)stream));
 }
 
+int attn_update_centroids(const attn_dims* dims, const void* k, const int32_t* seq_lens,
+                          const int32_t* prev_lens, int32_t span_hint, float* centroids, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!k || !centroids || span_hint < 1) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  return hip_status(skv::launch_update_centroids(k, seq_lens, prev_lens, centroids, dims->batch,
+                                                 dims->num_kv_heads, dims->head_dim, dims->max_blocks,
+                                                 dims->dtype, span_hint, (hipStream_t)stream));
+}
+
 int attn_score_centroids(const attn_dims* dims, const void* q, const float* centroids,
                          const int32_t* seq_lens, float* scores, void* stream) {
   int st = check_dims(dims);
@@ -164,6 +175,38 @@ int attn_select_topk(const attn_dims* dims, const float* scores, const int32_t* 
   return hip_status(skv::launch_topk(scores, seq_lens, dims->batch, dims->num_kv_heads, dims->max_blocks, k,
                                      n_sink_blocks, n_recent_blocks, max_sel, block_idx, n_sel,
                                      (hipStream_t)stream));
+}
+
+int attn_build_super_centroids(const attn_dims* dims, const float* centroids, const int32_t* seq_lens,
+                               int32_t group, float* super_centroids, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!centroids || !super_centroids || group < 1) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  return hip_status(skv::launch_super_centroids(centroids, seq_lens, super_centroids, dims->batch,
+                                                dims->num_kv_heads, dims->head_dim, dims->max_blocks, group,
+                                                (hipStream_t)stream));
+}
+
+int attn_select_two_level(const attn_dims* dims, const void* q, const float* centroids,
+                          const float* super_centroids, const int32_t* seq_lens, int32_t group,
+                          int32_t k_coarse, int32_t k, int32_t n_sink_blocks, int32_t n_recent_blocks,
+                          int32_t max_sel, int32_t* block_idx, int32_t* n_sel, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !centroids || !super_centroids || !block_idx || !n_sel) return ATTN_ERR_INVALID_ARG;
+  if (group < 1 || k_coarse < 0 || k < 0 || n_sink_blocks < 0 || n_recent_blocks < 0 || max_sel < 1)
+    return ATTN_ERR_INVALID_ARG;
+  const int64_t need = (int64_t)n_sink_blocks + n_recent_blocks + k;
+  if ((int64_t)max_sel < (need < dims->max_blocks ? need : (int64_t)dims->max_blocks)) return ATTN_ERR_INVALID_ARG;
+  const int64_t ns = ((int64_t)dims->max_blocks + group - 1) / group;
+  if (ns > skv::kTwoLevelMaxSuper) return ATTN_ERR_UNSUPPORTED;
+  if ((k_coarse < ns ? (int64_t)k_coarse : ns) * group > skv::kTwoLevelMaxCand) return ATTN_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return ATTN_OK;
+  return hip_status(skv::launch_two_level(q, centroids, super_centroids, seq_lens, dims->batch, dims->num_q_heads,
+                                          dims->num_kv_heads, dims->head_dim, dims->max_blocks, dims->dtype,
+                                          dims->scale, group, k_coarse, k, n_sink_blocks, n_recent_blocks, max_sel,
+                                          block_idx, n_sel, (hipStream_t)stream));
 }
 
 int attn_decode_sparse(const attn_dims* dims, const void* q, const void* k, const void* v,

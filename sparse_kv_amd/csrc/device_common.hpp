@@ -152,6 +152,6 @@ __device__ __forceinline__ float elem_f32(const T* p, int i) {
     return ((const float*)p)[i];
 }
 
-__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+__host__ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 }  // namespace skv

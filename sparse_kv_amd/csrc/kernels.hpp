@@ -44,6 +44,9 @@ hipError_t launch_merge(int32_t rows, int32_t S, int32_t d, const float* m, cons
 hipError_t launch_build_centroids(const void* k, const int32_t* seq_lens, float* c, int32_t B,
                                   int32_t Hkv, int32_t d, int32_t NBmax, int32_t dtype,
                                   hipStream_t st);
+hipError_t launch_update_centroids(const void* k, const int32_t* seq_lens, const int32_t* prev_lens, float* c,
+                                   int32_t B, int32_t Hkv, int32_t d, int32_t NBmax, int32_t dtype,
+                                   int32_t span_hint, hipStream_t st);
 hipError_t launch_score(const void* q, const float* c, const int32_t* seq_lens, float* scores,
                         int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t NBmax,
                         int32_t dtype, float scale, hipStream_t st);
@@ -51,6 +54,16 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int32_t B, 
                        int32_t NBmax, int32_t k, int32_t n_sink, int32_t n_recent,
                        int32_t max_sel, int32_t* idx, int32_t* n_sel, hipStream_t st);
 hipError_t launch_art(const ArtArgs& a, hipStream_t st);
+// Two-level selection capacities: super-blocks per sequence, and fine
+// candidates (k_coarse * group) inside the opened super-blocks.
+constexpr int32_t kTwoLevelMaxSuper = 4096;
+constexpr int32_t kTwoLevelMaxCand = 8192;
+hipError_t launch_super_centroids(const float* c, const int32_t* seq_lens, float* c2, int32_t B, int32_t Hkv,
+                                  int32_t d, int32_t NBmax, int32_t group, hipStream_t st);
+hipError_t launch_two_level(const void* q, const float* c, const float* c2, const int32_t* seq_lens, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t d, int32_t NBmax, int32_t dtype, float scale,
+                            int32_t group, int32_t k_coarse, int32_t k, int32_t n_sink, int32_t n_recent,
+                            int32_t max_sel, int32_t* idx, int32_t* n_sel, hipStream_t st);
 // Largest number of non-sink blocks a sequence may have for launch_order.
 constexpr int32_t kOrderMaxRest = 16384;
 hipError_t launch_order(const float* scores, const int32_t* seq_lens, int32_t B, int32_t Hkv,

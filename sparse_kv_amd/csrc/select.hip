@@ -15,18 +15,15 @@ namespace skv {
 namespace {
 
 // ---- centroids: one wave per block, row layout, fp32 sums ---------------
+// Centroid of block j of one (b, kv head) unit: the mean of its valid keys,
+// zeros for a block past the sequence's end.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void centroid_kernel(const void* __restrict__ k, const int32_t* __restrict__ seq_lens,
-                                                       float* __restrict__ C, int32_t Hkv, int32_t NBmax) {
+__device__ void centroid_block(const void* __restrict__ k, float* __restrict__ C, size_t unit, int j, int L,
+                               int32_t NBmax, int lane) {
   using Gm = Geo<T, D>;
   constexpr int E = Gm::E, CPR = Gm::CPR, TPI = Gm::TPI, ROWB = Gm::ROWB;
   constexpr bool BF = sizeof(T) == 2;
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (j >= NBmax) return;
-  const int g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
-  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
   const int nb = (L + kBlock - 1) / kBlock;
-  const size_t unit = (size_t)b * Hkv + g;
   float* crow = C + (unit * NBmax + j) * D;
   if (j >= nb) {
     for (int i = lane; i < D; i += 64) crow[i] = 0.f;
@@ -59,6 +56,44 @@ __global__ __launch_bounds__(256) void centroid_kernel(const void* __restrict__ 
 #pragma unroll
     for (int e = 0; e < E; ++e) crow[lane * E + e] = sum[e] / n;
   }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void centroid_kernel(const void* __restrict__ k, const int32_t* __restrict__ seq_lens,
+                                                       float* __restrict__ C, int32_t Hkv, int32_t NBmax) {
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= NBmax) return;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
+  centroid_block<T, D>(k, C, (size_t)b * Hkv + g, j, L, NBmax, threadIdx.x & 63);
+}
+
+// Refresh after tokens were appended: blocks [min(prev_len, L) / 64, nb) of
+// every row (the block that held the shorter end onwards), or only the last
+// block without previous lengths; blocks past the end are zeroed up to the
+// previous block count, so a shrunk row is cleared too.  Workgroup x of a
+// unit takes blocks lo + 4x + wave, lo + 4x + wave + 4X, ...
+template <typename T, int D>
+__global__ __launch_bounds__(256) void centroid_update_kernel(const void* __restrict__ k,
+                                                              const int32_t* __restrict__ seq_lens,
+                                                              const int32_t* __restrict__ prev_lens,
+                                                              float* __restrict__ C, int32_t Hkv, int32_t NBmax) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int Lmax = NBmax * kBlock;
+  const int L = clampi(seq_lens ? seq_lens[b] : Lmax, 0, Lmax);
+  const int nb = (L + kBlock - 1) / kBlock;
+  int lo, hi;
+  if (prev_lens) {
+    const int P = clampi(prev_lens[b], 0, Lmax);
+    lo = min(P, L) / kBlock;
+    hi = max(nb, (P + kBlock - 1) / kBlock);
+  } else {
+    lo = max(nb - 1, 0);
+    hi = nb;
+  }
+  const size_t unit = (size_t)b * Hkv + g;
+  for (int j = lo + blockIdx.x * 4 + (threadIdx.x >> 6); j < hi; j += gridDim.x * 4)
+    centroid_block<T, D>(k, C, unit, j, L, NBmax, threadIdx.x & 63);
 }
 
 // ---- scores: 4 waves x 32 centroid rows per workgroup -------------------
@@ -261,6 +296,241 @@ __global__ __launch_bounds__(1024) void order_kernel(const float* __restrict__ s
     out[i] = i == 0 ? (nb > 0 ? 0 : -1) : (i < nb ? (int32_t)(uint32_t)key[i - 1] : -1);
 }
 
+// ---- two-level selection ---------------------------------------------------
+// Super-block centroids from block centroids: the token-count-weighted mean
+// of the block means is the mean of the super-block's keys.
+template <int D>
+__global__ __launch_bounds__(256) void super_centroid_kernel(const float* __restrict__ C,
+                                                             const int32_t* __restrict__ seq_lens,
+                                                             float* __restrict__ C2, int32_t Hkv, int32_t NBmax,
+                                                             int32_t NSmax, int32_t group) {
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= NSmax) return;
+  const int g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
+  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
+  const int nb = (L + kBlock - 1) / kBlock;
+  const size_t unit = (size_t)b * Hkv + g;
+  float* out = C2 + (unit * NSmax + s) * D;
+  const int j0 = s * group, j1 = min(j0 + group, nb);
+  if (j0 >= j1) {
+    for (int c = lane; c < D; c += 64) out[c] = 0.f;
+    return;
+  }
+  const float* crow = C + (unit * NBmax) * D;
+  float acc[D / 64];
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+  for (int j = j0; j < j1; ++j) {
+    const float nj = (float)min(kBlock, L - j * kBlock);
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) acc[e] = fmaf(nj, crow[(size_t)j * D + lane + 64 * e], acc[e]);
+  }
+  const float n = (float)(min(L, j1 * kBlock) - j0 * kBlock);
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = acc[e] / n;
+}
+
+// Radix select (8 bits a pass, 256-thread workgroup) of the kk-th largest
+// key among items [0, n) with elig(i): returns that key and how many items
+// equal to it are to be taken (lowest indices first).  0 < kk < #eligible.
+template <typename KeyF, typename EligF>
+__device__ void radix_select(int n, int kk, KeyF key, EligF elig, uint32_t* hist, int* scan4, uint32_t* sh_prefix,
+                             int* sh_rem, uint32_t& thr, int& need_eq) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  int rem = kk;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      if (!elig(i)) continue;
+      const uint32_t u = key(i);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const int bin = 255 - tid;  // thread 0 takes the highest digit
+    const int x = (int)hist[bin];
+    int tot;
+    const int above = block_exscan(x, &tot, scan4);
+    if (above < rem && rem <= above + x) {
+      *sh_prefix = prefix | ((uint32_t)bin << shift);
+      *sh_rem = rem - above;
+    }
+    __syncthreads();
+    prefix = *sh_prefix;
+    rem = *sh_rem;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  thr = prefix;
+  need_eq = rem;
+}
+
+// Calls take(i, rank) for the kk best eligible items of [0, n) in index
+// order (rank = 0, 1, ... over the taken items), ties to the lower index.
+// Each thread owns a contiguous chunk, so ranks follow the index order.
+// Returns the number taken.
+template <typename KeyF, typename EligF, typename TakeF>
+__device__ int take_best(int n, int kk, KeyF key, EligF elig, TakeF take, uint32_t* hist, int* scan4,
+                         uint32_t* sh_prefix, int* sh_rem) {
+  const int tid = threadIdx.x;
+  const int CH = (n + 255) / 256;
+  const int i0 = min(tid * CH, n), i1 = min(i0 + CH, n);
+  int ne = 0;
+  for (int i = i0; i < i1; ++i) ne += elig(i) ? 1 : 0;
+  int n_elig;
+  block_exscan(ne, &n_elig, scan4);
+  const int kq = min(kk, n_elig);
+  const bool ranked = kq > 0 && kq < n_elig;
+  uint32_t thr = 0;
+  int need_eq = 0;
+  if (ranked) radix_select(n, kq, key, elig, hist, scan4, sh_prefix, sh_rem, thr, need_eq);
+  int eq_local = 0;
+  if (ranked)
+    for (int i = i0; i < i1; ++i)
+      if (elig(i) && key(i) == thr) ++eq_local;
+  int tot_eq;
+  const int eq_before = block_exscan(eq_local, &tot_eq, scan4);
+  auto chosen = [&](int i, int& eq_seen) -> bool {
+    if (kq == 0 || !elig(i)) return false;
+    if (!ranked) return true;
+    const uint32_t u = key(i);
+    if (u > thr) return true;
+    if (u == thr) return eq_seen++ < need_eq;
+    return false;
+  };
+  int eq_seen = eq_before, cnt = 0;
+  for (int i = i0; i < i1; ++i) cnt += chosen(i, eq_seen) ? 1 : 0;
+  int total;
+  int rank = block_exscan(cnt, &total, scan4);
+  eq_seen = eq_before;
+  for (int i = i0; i < i1; ++i)
+    if (chosen(i, eq_seen)) take(i, rank++);
+  __syncthreads();
+  return total;
+}
+
+// Scores n centroid rows against the LDS query qs: 16-byte loads, D/4 lanes
+// per row, and 8 load instructions in flight per wave before any reduction.
+// put(r, score) is called by one lane per row.
+template <int D, typename RowF, typename PutF>
+__device__ void score_rows(int n, const float* qs, RowF row_of, PutF put, float scale) {
+  constexpr int LPR = D / 4, RPI = 64 / LPR, NB8 = 8;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane % LPR, rsub = lane / LPR;
+  const f32x4 qv = *(const f32x4*)(qs + 4 * c);
+  for (int base = w * RPI * NB8; base < n; base += 4 * RPI * NB8) {
+    f32x4 x[NB8];
+#pragma unroll
+    for (int it = 0; it < NB8; ++it) {
+      const int r = base + it * RPI + rsub;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      x[it] = r < n ? *(const f32x4*)(row_of(r) + 4 * c) : z;
+    }
+#pragma unroll
+    for (int it = 0; it < NB8; ++it) {
+      float v = qv[0] * x[it][0];
+      v = fmaf(qv[1], x[it][1], v);
+      v = fmaf(qv[2], x[it][2], v);
+      v = fmaf(qv[3], x[it][3], v);
+      v = row16_sum(v);
+      if constexpr (LPR == 32) v = xrow16_sum(v);
+      const int r = base + it * RPI + rsub;
+      if (c == 0 && r < n) put(r, v * scale);
+    }
+  }
+}
+
+constexpr int kCoarseCap = kTwoLevelMaxSuper;
+constexpr int kCandCap = kTwoLevelMaxCand;
+
+// One 256-thread workgroup per (b, kv head): coarse scores of the super-
+// blocks that hold a non-forced block, the k_coarse best opened, fine scores
+// of the non-forced blocks inside them, the k best taken; forced sink and
+// window blocks added; ascending output, -1 padded.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void two_level_kernel(const void* __restrict__ q, const float* __restrict__ C,
+                                                        const float* __restrict__ C2,
+                                                        const int32_t* __restrict__ seq_lens, int32_t Hq,
+                                                        int32_t Hkv, int32_t NBmax, int32_t NSmax, int32_t group,
+                                                        int32_t k_coarse, int32_t k, int32_t n_sink,
+                                                        int32_t n_recent, int32_t max_sel, float scale,
+                                                        int32_t* __restrict__ idx, int32_t* __restrict__ n_sel) {
+  __shared__ __align__(16) float qs[D];
+  __shared__ float csc[kCoarseCap];
+  __shared__ unsigned char opened[kCoarseCap];
+  __shared__ int cand[kCandCap];
+  __shared__ float fsc[kCandCap];
+  __shared__ uint32_t hist[256];
+  __shared__ int scan4[4];
+  __shared__ uint32_t sh_prefix;
+  __shared__ int sh_rem;
+  const int unit = blockIdx.x, b = unit / Hkv, g = unit % Hkv;
+  const int tid = threadIdx.x;
+  const int G = Hq / Hkv;
+  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
+  const int nb = (L + kBlock - 1) / kBlock;
+  const int sink_hi = min(n_sink, nb);
+  const int rec_lo = max(nb - n_recent, sink_hi);
+  int32_t* out = idx + (size_t)unit * max_sel;
+
+  for (int c = tid; c < D; c += 256) {
+    float a = 0.f;
+    for (int h = 0; h < G; ++h) a += elem_f32((const T*)q + ((size_t)b * Hq + (size_t)g * G + h) * D, c);
+    qs[c] = a;
+  }
+  // super-blocks holding a block of [sink_hi, rec_lo) form the range [es0, es1)
+  const bool any = sink_hi < rec_lo;
+  const int es0 = any ? sink_hi / group : 0, es1 = any ? (rec_lo + group - 1) / group : 0;
+  const int nes = es1 - es0;
+  __syncthreads();
+  const float* C2u = C2 + (size_t)unit * NSmax * D;
+  score_rows<D>(
+      nes, qs, [&](int i) { return C2u + (size_t)(es0 + i) * D; }, [&](int i, float v) { csc[i] = v; }, scale);
+  for (int i = tid; i < nes; i += 256) opened[i] = 0;
+  __syncthreads();
+  auto all = [](int) { return true; };
+  take_best(
+      nes, k_coarse, [&](int i) { return score_key(csc[i]); }, all, [&](int i, int) { opened[i] = 1; }, hist,
+      scan4, &sh_prefix, &sh_rem);
+  // candidates: the non-forced blocks of the opened super-blocks, ascending
+  const int CH = (nes + 255) / 256;
+  const int i0 = min(tid * CH, nes), i1 = min(i0 + CH, nes);
+  auto m_lo = [&](int i) { return max((es0 + i) * group, sink_hi); };
+  auto m_hi = [&](int i) { return min((es0 + i + 1) * group, rec_lo); };
+  int cnt = 0;
+  for (int i = i0; i < i1; ++i)
+    if (opened[i]) cnt += m_hi(i) - m_lo(i);
+  int ncand;
+  int pos = block_exscan(cnt, &ncand, scan4);
+  for (int i = i0; i < i1; ++i)
+    if (opened[i])
+      for (int j = m_lo(i); j < m_hi(i); ++j)
+        if (pos < kCandCap) cand[pos++] = j;
+  ncand = min(ncand, kCandCap);
+  __syncthreads();
+  const float* Cu = C + (size_t)unit * NBmax * D;
+  score_rows<D>(
+      ncand, qs, [&](int i) { return Cu + (size_t)cand[i] * D; }, [&](int i, float v) { fsc[i] = v; }, scale);
+  __syncthreads();
+  const int npick = take_best(
+      ncand, k, [&](int i) { return score_key(fsc[i]); }, all,
+      [&](int i, int r) {
+        if (sink_hi + r < max_sel) out[sink_hi + r] = cand[i];
+      },
+      hist, scan4, &sh_prefix, &sh_rem);
+  for (int j = tid; j < sink_hi; j += 256)
+    if (j < max_sel) out[j] = j;
+  for (int j = rec_lo + tid; j < nb; j += 256) {
+    const int o = sink_hi + npick + (j - rec_lo);
+    if (o < max_sel) out[o] = j;
+  }
+  const int total = sink_hi + npick + (nb - rec_lo);
+  for (int o = total + tid; o < max_sel; o += 256) out[o] = -1;
+  if (tid == 0) n_sel[unit] = min(total, max_sel);
+}
+
 }  // namespace
 
 hipError_t launch_build_centroids(const void* k, const int32_t* seq_lens, float* c, int32_t B,
@@ -278,6 +548,26 @@ hipError_t launch_build_centroids(const void* k, const int32_t* seq_lens, float*
       centroid_kernel<float, 128><<<grid, 256, 0, st>>>(k, seq_lens, c, Hkv, NBmax);
     else
       centroid_kernel<float, 64><<<grid, 256, 0, st>>>(k, seq_lens, c, Hkv, NBmax);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_update_centroids(const void* k, const int32_t* seq_lens, const int32_t* prev_lens, float* c,
+                                   int32_t B, int32_t Hkv, int32_t d, int32_t NBmax, int32_t dtype,
+                                   int32_t span_hint, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  const int X = clampi((span_hint + 3) / 4, 1, (NBmax + 3) / 4);
+  const dim3 grid(X, Hkv, B);
+  if (dtype == 1) {
+    if (d == 128)
+      centroid_update_kernel<__bf16, 128><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax);
+    else
+      centroid_update_kernel<__bf16, 64><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax);
+  } else {
+    if (d == 128)
+      centroid_update_kernel<float, 128><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax);
+    else
+      centroid_update_kernel<float, 64><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax);
   }
   return hipGetLastError();
 }
@@ -307,6 +597,43 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int32_t B, 
   if (B == 0) return hipSuccess;
   topk_kernel<<<dim3(B * Hkv), 256, 0, st>>>(scores, seq_lens, Hkv, NBmax, k, n_sink, n_recent,
                                              max_sel, idx, n_sel);
+  return hipGetLastError();
+}
+
+hipError_t launch_super_centroids(const float* c, const int32_t* seq_lens, float* c2, int32_t B, int32_t Hkv,
+                                  int32_t d, int32_t NBmax, int32_t group, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  const int NS = (NBmax + group - 1) / group;
+  const dim3 grid((NS + 3) / 4, Hkv, B);
+  if (d == 128)
+    super_centroid_kernel<128><<<grid, 256, 0, st>>>(c, seq_lens, c2, Hkv, NBmax, NS, group);
+  else
+    super_centroid_kernel<64><<<grid, 256, 0, st>>>(c, seq_lens, c2, Hkv, NBmax, NS, group);
+  return hipGetLastError();
+}
+
+hipError_t launch_two_level(const void* q, const float* c, const float* c2, const int32_t* seq_lens, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t d, int32_t NBmax, int32_t dtype, float scale,
+                            int32_t group, int32_t k_coarse, int32_t k, int32_t n_sink, int32_t n_recent,
+                            int32_t max_sel, int32_t* idx, int32_t* n_sel, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  const int NS = (NBmax + group - 1) / group;
+  const dim3 grid(B * Hkv);
+#define SKV_TWO_LEVEL(T, D)                                                                                  \
+  two_level_kernel<T, D><<<grid, 256, 0, st>>>(q, c, c2, seq_lens, Hq, Hkv, NBmax, NS, group, k_coarse, k, \
+                                               n_sink, n_recent, max_sel, scale, idx, n_sel)
+  if (dtype == 1) {
+    if (d == 128)
+      SKV_TWO_LEVEL(__bf16, 128);
+    else
+      SKV_TWO_LEVEL(__bf16, 64);
+  } else {
+    if (d == 128)
+      SKV_TWO_LEVEL(float, 128);
+    else
+      SKV_TWO_LEVEL(float, 64);
+  }
+#undef SKV_TWO_LEVEL
   return hipGetLastError();
 }
 

@@ -96,6 +96,21 @@ def test_argument_validation(skv):
                                     None) == -1
     assert lib.attn_decode_art_list(ctypes.byref(d), *lst, FAKE, FAKE, 4, 1e-3, 1e-4, 0, 8, FAKE, FAKE, None,
                                     None) == -1
+    # centroid update: k, centroids and span_hint >= 1 are required
+    assert lib.attn_update_centroids(ctypes.byref(d), None, None, None, 1, FAKE, None) == -1
+    assert lib.attn_update_centroids(ctypes.byref(d), FAKE, None, None, 1, None, None) == -1
+    assert lib.attn_update_centroids(ctypes.byref(d), FAKE, None, None, 0, FAKE, None) == -1
+    # two-level selection: group >= 1, capacity limits, max_sel as for top-k
+    assert lib.attn_build_super_centroids(ctypes.byref(d), FAKE, None, 0, FAKE, None) == -1
+    assert lib.attn_build_super_centroids(ctypes.byref(d), None, None, 4, FAKE, None) == -1
+    tl = lambda dd, group, kc, k, ms: lib.attn_select_two_level(ctypes.byref(dd), FAKE, FAKE, FAKE, None, group, kc,
+                                                                k, 1, 1, ms, FAKE, FAKE, None)
+    assert tl(d, 0, 2, 2, 4) == -1
+    assert tl(d, 2, 2, 2, 3) == -1  # max_sel below sink + window + k
+    assert tl(d, 2, -1, 2, 4) == -1
+    assert tl(dims(max_blocks=4097 * 2), 2, 1, 1, 4) == -2  # more than 4096 super-blocks
+    assert tl(dims(max_blocks=16384), 16, 513, 1, 4) == -2  # 513 * 16 candidates
+    assert tl(dims(batch=0, max_blocks=8192), 16, 512, 1, 4) == 0
     # importance order: scores and order are required; at most 16384 blocks after the sink
     assert lib.attn_order_blocks(ctypes.byref(d), None, None, FAKE, None) == -1
     assert lib.attn_order_blocks(ctypes.byref(d), FAKE, None, None, None) == -1

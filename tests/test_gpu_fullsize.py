@@ -207,3 +207,42 @@ def test_importance_first_art_128k_batch8():
     for (b, g), (ro, rs) in ref.items():
         assert stop2[b, g * G:(g + 1) * G].tolist() == rs.tolist(), f"stop positions of unit ({b},{g})"
         assert_close(out2[b, g * G:(g + 1) * G], ro, TOL, f"importance-first ART unit ({b},{g})")
+
+
+def test_two_level_selection_128k_batch8():
+    """Two-level selection at 128K batch 8 (super-blocks of 16 blocks, 32 opened,
+    205 picks + sink + 64-block window) and decode over its lists."""
+    from oracle.selection import select_blocks_two_level, super_centroids, two_level_gaps
+
+    W = synth.WORKLOADS[3]
+    B, Hq, Hkv, d, L = W["B"], W["Hq"], W["Hkv"], W["d"], W["L"]
+    k_top, ns, nr = W["topk"], W["n_sink"], W["n_recent"]
+    group, kc = 16, 32
+    inp = synth.make_inputs(3, B, Hq, Hkv, d, L, kind="mixture")
+    import sparse_kv_amd as skv
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    C = skv.attn_build_centroids(k)
+    C2 = skv.attn_build_super_centroids(C, group)
+    idx, n = skv.attn_select_two_level(q, C, C2, group, None, k_coarse=kc, k=k_top, n_sink_blocks=ns, n_recent_blocks=nr)
+    sp = skv.attn_merge_states(*skv.attn_decode_sparse(q, k, v, idx, n, None, num_splits=4))
+    torch.cuda.synchronize()
+    idx, n, sp = idx.cpu().numpy(), n.cpu().numpy(), sp.cpu().numpy()
+    assert (n == ns + nr + k_top).all()
+    G = Hq // Hkv
+    nb = L // 64
+    checked = 0
+    for b, g in SAMPLE:
+        qf, kf, vf, seq = unit_f64(inp, b, g)
+        fine = oracle.centroid_scores(qf, oracle.block_centroids(kf, seq), seq, inp.scale)[0, 0]
+        coarse = oracle.centroid_scores(qf, super_centroids(kf, seq, group), seq, inp.scale, block=64 * group)[0, 0]
+        cg, fg = two_level_gaps(fine, coarse, nb, group, kc, k_top, ns, nr)
+        log(f"  unit ({b},{g}): coarse gap {cg:.2e}, fine gap {fg:.2e}")
+        if min(cg, fg) > 1e-4:
+            ref = select_blocks_two_level(fine, coarse, nb, group, kc, k_top, ns, nr)
+            assert idx[b, g, :n[b, g]].tolist() == ref, f"two-level blocks of unit ({b},{g})"
+            checked += 1
+        got = [[idx[b, g, :n[b, g]].tolist()]]
+        assert_close(sp[b, g * G:(g + 1) * G], oracle.decode_blocks(qf, kf, vf, seq, inp.scale, got)[0], TOL,
+                     f"decode over the two-level list, unit ({b},{g})")
+    assert checked >= 2, "too few sampled units with clear two-level margins"

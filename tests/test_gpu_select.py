@@ -176,3 +176,108 @@ def test_squeezed_worked_example_on_gpu():
         np.float32).astype(np.float64)
     want = oracle.decode_blocks(qf[None, None], Kf[None, None], Vf[None, None], np.array([128]), 1 / 8.0, [[[1]]])
     assert_close(out.cpu().numpy(), want, 1e-5, "cluster-2-only output")
+
+
+@pytest.mark.parametrize("dt,d,hint", [("bf16", 128, 4), ("f32", 64, 1)])
+def test_centroid_update_after_appends(dt, d, hint):
+    """Centroids built at earlier lengths and refreshed after appends (or a
+    shrink) equal the oracle's at the new lengths; blocks before the refreshed
+    range are not written."""
+    import sparse_kv_amd as skv
+
+    log(f"[select] centroid update {dt} d={d} span_hint={hint}")
+    NB = 12
+    new = np.array([64 * 12, 64 * 5 + 3, 64 * 7, 40, 64 * 5 + 3, 0], dtype=np.int32)
+    old = np.array([64 * 9 + 10, 64 * 5 + 2, 64 * 6, 0, 64 * 8, 0], dtype=np.int32)
+    lo = np.minimum(old, new) // 64
+    inp = synth.make_inputs(31, 6, 4, 2, d, 64 * NB, dtype=dt, kind="mixture", seq_lens=new)
+    q, k, v, sl = upload(inp)
+    old_t = torch.from_numpy(old).cuda()
+    C = skv.attn_build_centroids(k, old_t)
+    for b in range(6):
+        C[b, :, :lo[b]] = 123.0  # sentinel: outside the refreshed range
+    skv.attn_update_centroids(k, C, sl, prev_lens=old_t, span_hint=hint)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    _, kf, _ = inp.f64()
+    ref = oracle.block_centroids(kf, inp.seq_lens)
+    for b in range(6):
+        assert (got[b, :, :lo[b]] == 123.0).all(), f"row {b}: a block before the range was written"
+        assert_close(got[b, :, lo[b]:], ref[b, :, lo[b]:], 1e-5, f"row {b} refreshed blocks")
+
+    log("  one token appended per row, last block only")
+    new1 = np.array([64 * 7, 64 * 7 + 1, 1, 64 * 12, 64 * 3 + 30, 65], dtype=np.int32)
+    inp = synth.make_inputs(32, 6, 4, 2, d, 64 * NB, dtype=dt, kind="mixture", seq_lens=new1)
+    q, k, v, sl = upload(inp)
+    C = skv.attn_build_centroids(k, torch.from_numpy(new1 - 1).cuda())
+    skv.attn_update_centroids(k, C, sl, span_hint=hint)
+    torch.cuda.synchronize()
+    _, kf, _ = inp.f64()
+    assert_close(C.cpu().numpy(), oracle.block_centroids(kf, inp.seq_lens), 1e-5, "after one-token appends")
+
+
+@pytest.mark.parametrize("dt,d,group,seq", [("bf16", 128, 4, [64 * 30, 64 * 13 + 5, 0]),
+                                           ("f32", 64, 3, [64 * 30, 1, 64 * 7])])
+def test_super_centroids(dt, d, group, seq):
+    import sparse_kv_amd as skv
+
+    log(f"[select] super-block centroids {dt} d={d} group={group}")
+    inp = synth.make_inputs(33, 3, 4, 2, d, 64 * 30, dtype=dt, kind="mixture", seq_lens=seq)
+    q, k, v, sl = upload(inp)
+    C2 = skv.attn_build_super_centroids(skv.attn_build_centroids(k, sl), group, sl)
+    torch.cuda.synchronize()
+    _, kf, _ = inp.f64()
+    assert_close(C2.cpu().numpy(), oracle.selection.super_centroids(kf, inp.seq_lens, group), 1e-5, "super centroids")
+
+
+def two_level_inputs(cfg, B, Hq, Hkv, d, L, seq, group, kc, k, ns, nr, dtype="bf16"):
+    """Mixture inputs whose two decision boundaries clear 1e-4 (units redrawn)."""
+    from oracle.selection import select_all_two_level, super_centroids, two_level_gaps
+
+    attempts = {}
+    for _ in range(30):
+        inp = synth.make_inputs(cfg, B, Hq, Hkv, d, L, dtype=dtype, kind="mixture", seq_lens=seq, attempts=attempts)
+        qf, kf, _ = inp.f64()
+        fine = oracle.centroid_scores(qf, oracle.block_centroids(kf, inp.seq_lens), inp.seq_lens, inp.scale)
+        coarse = oracle.centroid_scores(qf, super_centroids(kf, inp.seq_lens, group), inp.seq_lens, inp.scale,
+                                        block=64 * group)
+        bad = []
+        for b in range(B):
+            nb = -(-int(inp.seq_lens[b]) // 64)
+            for g in range(Hkv):
+                if min(two_level_gaps(fine[b, g], coarse[b, g], nb, group, kc, k, ns, nr)) <= 1e-4:
+                    bad.append((b, g))
+        if not bad:
+            return inp, select_all_two_level(fine, coarse, inp.seq_lens, group, kc, k, ns, nr)
+        for u in bad:
+            attempts[u] = attempts.get(u, 0) + 1
+    raise AssertionError("could not draw inputs with two-level selection margins")
+
+
+@pytest.mark.parametrize("label,group,kc,k,ns,nr,seq", [
+    ("g4 open 3 of 8", 4, 3, 5, 1, 2, [64 * 32, 64 * 21 + 7]),
+    ("g8 open 1", 8, 1, 3, 1, 4, [64 * 32, 64 * 32]),
+    ("g3 open all = one level", 3, 100, 7, 1, 1, [64 * 32, 64 * 17]),
+    ("g5 forced only", 5, 0, 4, 2, 3, [64 * 32, 64 * 4]),
+    ("g4 short rows", 4, 2, 6, 1, 1, [64 * 2 + 1, 0]),
+    ("g16 window covers most", 16, 2, 8, 1, 20, [64 * 32, 64 * 25]),
+])
+def test_two_level_selection_exact(label, group, kc, k, ns, nr, seq):
+    import sparse_kv_amd as skv
+
+    log(f"[select] two-level: {label}")
+    inp, lists = two_level_inputs(34, 2, 8, 2, 128, 64 * 32, seq, group, kc, k, ns, nr)
+    q, kk, v, sl = upload(inp)
+    C = skv.attn_build_centroids(kk, sl)
+    C2 = skv.attn_build_super_centroids(C, group, sl)
+    idx, n = skv.attn_select_two_level(q, C, C2, group, sl, k_coarse=kc, k=k, n_sink_blocks=ns, n_recent_blocks=nr)
+    torch.cuda.synchronize()
+    idx, n = idx.cpu().numpy(), n.cpu().numpy()
+    for b in range(2):
+        for g in range(2):
+            assert idx[b, g, :n[b, g]].tolist() == lists[b][g], (b, g)
+            assert (idx[b, g, n[b, g]:] == -1).all()
+    if kc >= 100:
+        one = skv.attn_select_topk(skv.attn_score_centroids(q, C, sl), sl, k=k, n_sink_blocks=ns, n_recent_blocks=nr)
+        torch.cuda.synchronize()
+        assert np.array_equal(one[0].cpu().numpy(), idx) and np.array_equal(one[1].cpu().numpy(), n)
