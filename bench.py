@@ -14,6 +14,8 @@ Optional (--stages ...,art_imp): centroid scores + importance order + ART
 visiting block 0 then blocks by descending centroid score.  Optional
 (--stages ...,sparse2): two-level selection (super-blocks of 16 blocks, 32
 opened, then the same 205 picks + sink + window) + listed-block decode + merge.
+Optional (--stages ...,dense_paged): the dense stage over a paged cache whose
+blocks sit in a randomly permuted pool, addressed through a block table.
 Block centroids are built once before timing (they change only when a block
 fills).  Each stage reads its own copy of the KV cache so that no stage is
 served from the 256 MB last-level cache filled by the previous one.
@@ -74,7 +76,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", default="dense,sparse,art,window",
-                    help="comma list of dense, sparse, art, window, art_imp, sparse2")
+                    help="comma list of dense, sparse, art, window, art_imp, sparse2, dense_paged")
     ap.add_argument("--splits-per-shard", type=int, default=4, help="hybrid256k: inner splits per context shard")
     ap.add_argument("--sa-splits", type=int, default=32, help="hybrid256k: splits of a sink+window layer")
     ap.add_argument("--workload", default="decode128k", choices=["decode128k", "art64k", "hybrid256k"],
@@ -133,6 +135,18 @@ def main():
     C = skv.attn_build_centroids(copies["sparse"][0]) if "sparse" in stages else None
     c_ev[1].record()
     C_imp = skv.attn_build_centroids(copies["art_imp"][0]) if "art_imp" in stages else None
+    if "dense_paged" in stages:
+        # pool[perm[i]] = logical block i (row-major over (b, j)); table[b, j] = perm[b * NB + j]
+        perm = torch.randperm(B * NB, generator=torch.Generator().manual_seed(5), dtype=torch.int64).to(dev)
+
+        def to_pool(x):
+            blocks = x.view(B, Hkv, NB, 64, d).permute(0, 2, 1, 3, 4).reshape(B * NB, Hkv, 64, d)
+            pool = torch.empty_like(blocks)
+            pool[perm] = blocks
+            return pool
+
+        kpool, vpool = to_pool(k0), to_pool(v0)
+        ptable = perm.view(B, NB).to(torch.int32).contiguous()
     group2, kc2 = 16, 32
     C_2 = skv.attn_build_centroids(copies["sparse2"][0]) if "sparse2" in stages else None
     C2_2 = skv.attn_build_super_centroids(C_2, group2) if "sparse2" in stages else None
@@ -147,6 +161,8 @@ def main():
     st_s = (torch.empty((B, Hq, Ss), **f32), torch.empty((B, Hq, Ss), **f32), torch.empty((B, Hq, Ss, d), **f32))
     st_w = (torch.empty((B, Hq, Sw), **f32), torch.empty((B, Hq, Sw), **f32), torch.empty((B, Hq, Sw, d), **f32))
     out_d, out_s, out_w, out_a = (torch.empty((B, Hq, d), **f32) for _ in range(4))
+    st_p = (torch.empty((B, Hq, S), **f32), torch.empty((B, Hq, S), **f32), torch.empty((B, Hq, S, d), **f32))
+    out_p = torch.empty((B, Hq, d), **f32)
     scores = torch.empty((B, Hkv, NB), **f32)
     max_sel = n_sink + n_recent + topk
     sel_idx = torch.empty((B, Hkv, max_sel), dtype=torch.int32, device=dev)
@@ -201,6 +217,12 @@ def main():
             skv.attn_decode_sparse(q, kw, vw, win_idx, win_n, None, num_splits=Sw, m=st_w[0], l=st_w[1], o=st_w[2])
             skv.attn_merge_states(*st_w, out=out_w)
             mark("window.1")
+        if "dense_paged" in stages:
+            mark("dense_paged.0")
+            skv.attn_decode_dense_paged(q, kpool, vpool, ptable, None, num_splits=S, m=st_p[0], l=st_p[1], o=st_p[2])
+            mark("dense_paged.k")
+            skv.attn_merge_states(*st_p, out=out_p)
+            mark("dense_paged.1")
         if "sparse2" in stages:
             k2, v2 = copies["sparse2"]
             mark("sparse2.0")
@@ -273,6 +295,14 @@ def main():
         by = float(win_n.cpu().numpy().sum()) * kv_block + q_bytes + o_bytes
         total_bytes += by
         paths["window"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), tokens_per_s=B / (ms * 1e-3), splits=Sw)
+    if "dense_paged" in stages:
+        ms = avg_ms("dense_paged.0", "dense_paged.1")
+        by = units * NB * kv_block + q_bytes + o_bytes + B * NB * 4
+        total_bytes += by
+        paths["dense_paged"] = dict(ms=ms, kernel_ms=avg_ms("dense_paged.0", "dense_paged.k"), bytes=by,
+                                    gbs=gbs(by, ms), tokens_per_s=B / (ms * 1e-3), splits=S)
+        if "dense" in stages:
+            paths["dense_paged"]["max_abs_diff_vs_contiguous"] = float((out_p - out_d).abs().max())
     if "sparse2" in stages:
         n2 = sel2_n.cpu().numpy()
         ms = avg_ms("sparse2.0", "sparse2.1")
@@ -306,7 +336,7 @@ def main():
             if "art" in stages:
                 paths["art"]["max_abs_err_vs_dense"] = float((out_a.double() - ref).abs().max())
     if "dense" in paths:
-        for k_ in ("sparse", "art", "window", "art_imp", "sparse2"):
+        for k_ in ("sparse", "art", "window", "art_imp", "sparse2", "dense_paged"):
             if k_ in paths:
                 paths[k_]["speedup_vs_dense"] = paths["dense"]["ms"] / paths[k_]["ms"]
 

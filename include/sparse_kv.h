@@ -212,6 +212,45 @@ int attn_decode_sparse(const attn_dims* dims, const void* q, const void* k, cons
                        void* stream);
 
 /*
+ * A paged KV cache.  Every (block, kv head) run of 64 tokens is contiguous in
+ * a pool shared by the batch rows; a block table maps each row's logical
+ * blocks to pool blocks (rows may share pool blocks, e.g. a common prefix).
+ * The pages organise the cache in 64-token blocks ("ART" summary, §2.1) and
+ * move whole blocks ("SparDA" summary, offloaded KV blocks); the layout is
+ * this library's.
+ *   k_pool, v_pool  [pool_blocks, Hkv, 64, d] in the dims' dtype (v_pool may
+ *                   be NULL where only K is read).
+ *   block_table     int32 [B, table_stride], device memory: entry j of row b
+ *                   is the pool block of logical block j, for j < nb(b)
+ *                   (precondition: in [0, pool_blocks); entries are clamped).
+ *   table_stride    >= max_blocks.
+ * The paged entry points compute exactly what their contiguous namesakes
+ * compute on the cache the table describes; dims.max_blocks is the logical
+ * block capacity of a row.  Invalid descriptors give ATTN_ERR_INVALID_ARG.
+ */
+typedef struct {
+  const void* k_pool;
+  const void* v_pool;
+  int64_t pool_blocks;
+  const int32_t* block_table;
+  int32_t table_stride;
+} attn_paged_kv;
+
+int attn_decode_dense_paged(const attn_dims* dims, const void* q, const attn_paged_kv* kv, const int32_t* seq_lens,
+                            int32_t block_begin, int32_t block_end, int32_t num_splits, float* m, float* l,
+                            float* o, void* stream);
+int attn_decode_sparse_paged(const attn_dims* dims, const void* q, const attn_paged_kv* kv,
+                             const int32_t* seq_lens, const int32_t* block_idx, const int32_t* n_sel,
+                             int32_t max_sel, int32_t num_splits, float* m, float* l, float* o, void* stream);
+int attn_build_centroids_paged(const attn_dims* dims, const attn_paged_kv* kv, const int32_t* seq_lens,
+                               float* centroids, void* stream);
+int attn_update_centroids_paged(const attn_dims* dims, const attn_paged_kv* kv, const int32_t* seq_lens,
+                                const int32_t* prev_lens, int32_t span_hint, float* centroids, void* stream);
+int attn_decode_art_paged(const attn_dims* dims, const void* q, const attn_paged_kv* kv, const int32_t* seq_lens,
+                          const int32_t* order, float tau, float phi, int32_t patience, int32_t probe_dim,
+                          float* out, int32_t* stop_pos, int32_t* blocks_fetched, void* stream);
+
+/*
  * Decode attention with ART run-time termination.
  * Defines: "ART (Attention Run-time Termination)" summary, §2.1-2.4.  Blocks
  * are folded into the running state in a visit order; after folding the

@@ -37,6 +37,11 @@ EXPORTS = (
     "attn_decode_art",
     "attn_decode_art_list",
     "attn_order_blocks",
+    "attn_decode_dense_paged",
+    "attn_decode_sparse_paged",
+    "attn_build_centroids_paged",
+    "attn_update_centroids_paged",
+    "attn_decode_art_paged",
     "attn_decode_routed",
     "attn_routed_workspace_bytes",
     "attn_status_string",
@@ -56,10 +61,21 @@ class AttnDims(ctypes.Structure):
     ]
 
 
+class AttnPagedKV(ctypes.Structure):
+    _fields_ = [
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("pool_blocks", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p),
+        ("table_stride", ctypes.c_int32),
+    ]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _F = ctypes.c_float
 _D = ctypes.POINTER(AttnDims)
+_K = ctypes.POINTER(AttnPagedKV)
 _SIG = {
     "attn_decode_dense": [_D, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
     "attn_merge_states": [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P],
@@ -73,6 +89,11 @@ _SIG = {
     "attn_decode_art": [_D, _P, _P, _P, _P, _P, _F, _F, _I, _I, _P, _P, _P, _P],
     "attn_decode_art_list": [_D, _P, _P, _P, _P, _P, _P, _I, _F, _F, _I, _I, _P, _P, _P, _P],
     "attn_order_blocks": [_D, _P, _P, _P, _P],
+    "attn_decode_dense_paged": [_D, _P, _K, _P, _I, _I, _I, _P, _P, _P, _P],
+    "attn_decode_sparse_paged": [_D, _P, _K, _P, _P, _P, _I, _I, _P, _P, _P, _P],
+    "attn_build_centroids_paged": [_D, _K, _P, _P, _P],
+    "attn_update_centroids_paged": [_D, _K, _P, _P, _I, _P, _P],
+    "attn_decode_art_paged": [_D, _P, _K, _P, _P, _F, _F, _I, _I, _P, _P, _P, _P],
     "attn_decode_routed": [_D, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _P, ctypes.c_size_t, _P, _P],
     "attn_routed_workspace_bytes": [_D, _I, _I, _I],
 }
@@ -516,3 +537,123 @@ def attn_decode_routed(qs, ks, vs, route_mask, seq_lens=None, n_shards=8, splits
                                      _stream(dev))
     _check(st, "attn_decode_routed")
     return outs
+
+
+# ---- paged cache ----------------------------------------------------------
+
+def _paged(k_pool, v_pool, block_table, device):
+    """(AttnPagedKV, Hkv, NBmax, d, dtype code) from pools [P, Hkv, 64, d] and a table [B, NBmax]."""
+    _need(k_pool, "k_pool", device)
+    if k_pool.dim() != 4 or k_pool.shape[2] != BLOCK:
+        raise ValueError(f"k_pool must be [pool_blocks, Hkv, {BLOCK}, d]")
+    if v_pool is not None:
+        _need(v_pool, "v_pool", device, k_pool.dtype, k_pool.shape)
+    _need(block_table, "block_table", device, torch.int32)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_blocks]")
+    P, Hkv, _, d = k_pool.shape
+    kv = AttnPagedKV(k_pool.data_ptr(), None if v_pool is None else v_pool.data_ptr(), P, block_table.data_ptr(),
+                     block_table.shape[1])
+    return kv, Hkv, block_table.shape[1], d, _dtype_code(k_pool)
+
+
+def _paged_dims(q, k_pool, v_pool, block_table, scale):
+    dev = q.device
+    _need(q, "q", dev)
+    kv, Hkv, NBmax, d, code = _paged(k_pool, v_pool, block_table, dev)
+    if q.dim() != 3 or q.shape[2] != d or q.shape[0] != block_table.shape[0]:
+        raise ValueError("q must be [B, Hq, d] with B = block_table rows")
+    if q.dtype != k_pool.dtype:
+        raise ValueError("q and the pools must share one dtype")
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    return AttnDims(q.shape[0], q.shape[1], Hkv, d, BLOCK, NBmax, code, s), kv
+
+
+def attn_decode_dense_paged(q, k_pool, v_pool, block_table, seq_lens=None, num_splits=16, block_begin=0,
+                            block_end=-1, scale=None, m=None, l=None, o=None):
+    """attn_decode_dense over a paged cache: per-split states (m, l, o)."""
+    dev = q.device
+    dims, kv = _paged_dims(q, k_pool, v_pool, block_table, scale)
+    seq = _seq(seq_lens, dims.batch, dev)
+    rows = (dims.batch, dims.num_q_heads, int(num_splits))
+    m = _out(m, rows, torch.float32, dev, "m")
+    l = _out(l, rows, torch.float32, dev, "l")
+    o = _out(o, rows + (dims.head_dim,), torch.float32, dev, "o")
+    with _on_device(dev):
+        st = lib().attn_decode_dense_paged(ctypes.byref(dims), _ptr(q), ctypes.byref(kv), _ptr(seq),
+                                          int(block_begin), int(block_end), int(num_splits), _ptr(m), _ptr(l),
+                                          _ptr(o), _stream(dev))
+    _check(st, "attn_decode_dense_paged")
+    return m, l, o
+
+
+def attn_decode_sparse_paged(q, k_pool, v_pool, block_table, block_idx, n_sel, seq_lens=None, num_splits=4,
+                             scale=None, m=None, l=None, o=None):
+    """attn_decode_sparse over a paged cache: per-split states over the listed blocks."""
+    dev = q.device
+    dims, kv = _paged_dims(q, k_pool, v_pool, block_table, scale)
+    _need(block_idx, "block_idx", dev, torch.int32)
+    if block_idx.dim() != 3 or tuple(block_idx.shape[:2]) != (dims.batch, dims.num_kv_heads):
+        raise ValueError("block_idx must be [B, Hkv, max_sel]")
+    _need(n_sel, "n_sel", dev, torch.int32, (dims.batch, dims.num_kv_heads))
+    seq = _seq(seq_lens, dims.batch, dev)
+    rows = (dims.batch, dims.num_q_heads, int(num_splits))
+    m = _out(m, rows, torch.float32, dev, "m")
+    l = _out(l, rows, torch.float32, dev, "l")
+    o = _out(o, rows + (dims.head_dim,), torch.float32, dev, "o")
+    with _on_device(dev):
+        st = lib().attn_decode_sparse_paged(ctypes.byref(dims), _ptr(q), ctypes.byref(kv), _ptr(seq),
+                                           _ptr(block_idx), _ptr(n_sel), int(block_idx.shape[2]), int(num_splits),
+                                           _ptr(m), _ptr(l), _ptr(o), _stream(dev))
+    _check(st, "attn_decode_sparse_paged")
+    return m, l, o
+
+
+def attn_build_centroids_paged(k_pool, block_table, seq_lens=None, out=None):
+    """Block centroids [B, Hkv, NBmax, d] of a paged cache."""
+    dev = k_pool.device
+    kv, Hkv, NBmax, d, code = _paged(k_pool, None, block_table, dev)
+    B = block_table.shape[0]
+    dims = AttnDims(B, Hkv, Hkv, d, BLOCK, NBmax, code, 1.0)
+    seq = _seq(seq_lens, B, dev)
+    out = _out(out, (B, Hkv, NBmax, d), torch.float32, dev, "out")
+    with _on_device(dev):
+        st = lib().attn_build_centroids_paged(ctypes.byref(dims), ctypes.byref(kv), _ptr(seq), _ptr(out),
+                                             _stream(dev))
+    _check(st, "attn_build_centroids_paged")
+    return out
+
+
+def attn_update_centroids_paged(k_pool, block_table, centroids, seq_lens=None, prev_lens=None, span_hint=1):
+    """attn_update_centroids over a paged cache (centroids updated in place)."""
+    dev = k_pool.device
+    kv, Hkv, NBmax, d, code = _paged(k_pool, None, block_table, dev)
+    B = block_table.shape[0]
+    _need(centroids, "centroids", dev, torch.float32, (B, Hkv, NBmax, d))
+    dims = AttnDims(B, Hkv, Hkv, d, BLOCK, NBmax, code, 1.0)
+    seq = _seq(seq_lens, B, dev)
+    prev = None if prev_lens is None else _need(prev_lens, "prev_lens", dev, torch.int32, (B,))
+    with _on_device(dev):
+        st = lib().attn_update_centroids_paged(ctypes.byref(dims), ctypes.byref(kv), _ptr(seq), _ptr(prev),
+                                              int(span_hint), _ptr(centroids), _stream(dev))
+    _check(st, "attn_update_centroids_paged")
+    return centroids
+
+
+def attn_decode_art_paged(q, k_pool, v_pool, block_table, seq_lens=None, order=None, tau=1e-3, phi=1e-4,
+                          patience=2, probe_dim=8, scale=None, out=None, stop_pos=None, blocks_fetched=None):
+    """attn_decode_art over a paged cache: (out, stop_pos, blocks_fetched)."""
+    dev = q.device
+    dims, kv = _paged_dims(q, k_pool, v_pool, block_table, scale)
+    seq = _seq(seq_lens, dims.batch, dev)
+    if order is not None:
+        _need(order, "order", dev, torch.int32, (dims.batch, dims.num_kv_heads, dims.max_blocks))
+    out = _out(out, (dims.batch, dims.num_q_heads, dims.head_dim), torch.float32, dev, "out")
+    stop_pos = _out(stop_pos, (dims.batch, dims.num_q_heads), torch.int32, dev, "stop_pos")
+    blocks_fetched = _out(blocks_fetched, (dims.batch, dims.num_kv_heads), torch.int32, dev, "blocks_fetched")
+    with _on_device(dev):
+        st = lib().attn_decode_art_paged(ctypes.byref(dims), _ptr(q), ctypes.byref(kv), _ptr(seq), _ptr(order),
+                                        float(tau), float(phi), int(patience), int(probe_dim), _ptr(out),
+                                        _ptr(stop_pos), _ptr(blocks_fetched), _stream(dev))
+    _check(st, "attn_decode_art_paged")
+    return out, stop_pos, blocks_fetched

@@ -23,8 +23,8 @@ int check_dims(const attn_dims* d) {
   if (d->head_dim != 64 && d->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (d->block_size != 64) return ATTN_ERR_UNSUPPORTED;
   if (d->num_q_heads / d->num_kv_heads > 8) return ATTN_ERR_UNSUPPORTED;
-  // one (b, kv head) slice of K or V is addressed with 32-bit buffer offsets;
-  // offsets from 2 GiB up are reserved as "no block" (reads return zeros)
+  // one (b, kv head) slice of K or V is one buffer resource, whose range
+  // (the slice's valid bytes) is a signed 32-bit field
   const uint64_t row_bytes = (uint64_t)d->head_dim * (d->dtype == ATTN_BF16 ? 2 : 4);
   if ((uint64_t)d->max_blocks * 64 * row_bytes > (1ull << 31)) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
@@ -83,6 +83,22 @@ RoutedLayout routed_layout(const attn_dims* d, int32_t n_shards, int32_t sps, in
   return r;
 }
 
+// Paged cache: the pools, the pool size and the table must be given, and the
+// table must hold a row of at least max_blocks entries.
+int check_paged(const attn_dims* d, const attn_paged_kv* kv, bool need_v) {
+  if (!kv || !kv->k_pool || (need_v && !kv->v_pool) || !kv->block_table) return ATTN_ERR_INVALID_ARG;
+  if (kv->pool_blocks < 1 || kv->table_stride < d->max_blocks) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+void set_paged(skv::DecodeArgs& a, const attn_paged_kv* kv) {
+  a.k = kv->k_pool;
+  a.v = kv->v_pool;
+  a.table = kv->block_table;
+  a.table_stride = kv->table_stride;
+  a.pool_blocks = kv->pool_blocks;
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,6 +134,39 @@ int attn_decode_dense(const attn_dims* dims, const void* q, const void* k, const
   return hip_status(skv::launch_decode(a, false, (hipStream_t)stream));
 }
 
+int attn_decode_dense_paged(const attn_dims* dims, const void* q, const attn_paged_kv* kv, const int32_t* seq_lens,
+                            int32_t block_begin, int32_t block_end, int32_t num_splits, float* m, float* l,
+                            float* o, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_paged(dims, kv, true))) return st;
+  if (!q || !m || !l || !o) return ATTN_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > (1 << 24) || block_begin < 0) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  skv::DecodeArgs a = decode_args(dims, q, nullptr, nullptr, seq_lens, num_splits, m, l, o);
+  set_paged(a, kv);
+  a.block_begin = block_begin;
+  a.block_end = block_end;
+  return hip_status(skv::launch_decode(a, false, (hipStream_t)stream));
+}
+
+int attn_decode_sparse_paged(const attn_dims* dims, const void* q, const attn_paged_kv* kv,
+                             const int32_t* seq_lens, const int32_t* block_idx, const int32_t* n_sel,
+                             int32_t max_sel, int32_t num_splits, float* m, float* l, float* o, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_paged(dims, kv, true))) return st;
+  if (!q || !block_idx || !n_sel || !m || !l || !o) return ATTN_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > (1 << 24) || max_sel < 1) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  skv::DecodeArgs a = decode_args(dims, q, nullptr, nullptr, seq_lens, num_splits, m, l, o);
+  set_paged(a, kv);
+  a.block_idx = block_idx;
+  a.n_sel = n_sel;
+  a.max_sel = max_sel;
+  return hip_status(skv::launch_decode(a, true, (hipStream_t)stream));
+}
+
 int attn_merge_states(int32_t rows, int32_t num_splits, int32_t head_dim, const float* m,
                       const float* l, const float* o, float* out, float* m_out, float* l_out,
                       void* stream) {
@@ -138,6 +187,32 @@ int attn_build_centroids(const attn_dims* dims, const void* k, const int32_t* se
   return hip_status(skv::launch_build_centroids(k, seq_lens, centroids, dims->batch, dims->num_kv_heads,
                                                 dims->head_dim, dims->max_blocks, dims->dtype,
                                                 (hipStream_t)stream));
+}
+
+int attn_build_centroids_paged(const attn_dims* dims, const attn_paged_kv* kv, const int32_t* seq_lens,
+                               float* centroids, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_paged(dims, kv, false))) return st;
+  if (!centroids) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  const skv::PagedK pg{kv->block_table, kv->table_stride, kv->pool_blocks};
+  return hip_status(skv::launch_build_centroids(kv->k_pool, seq_lens, centroids, dims->batch, dims->num_kv_heads,
+                                                dims->head_dim, dims->max_blocks, dims->dtype,
+                                                (hipStream_t)stream, pg));
+}
+
+int attn_update_centroids_paged(const attn_dims* dims, const attn_paged_kv* kv, const int32_t* seq_lens,
+                                const int32_t* prev_lens, int32_t span_hint, float* centroids, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_paged(dims, kv, false))) return st;
+  if (!centroids || span_hint < 1) return ATTN_ERR_INVALID_ARG;
+  if (dims->batch == 0) return ATTN_OK;
+  const skv::PagedK pg{kv->block_table, kv->table_stride, kv->pool_blocks};
+  return hip_status(skv::launch_update_centroids(kv->k_pool, seq_lens, prev_lens, centroids, dims->batch,
+                                                 dims->num_kv_heads, dims->head_dim, dims->max_blocks,
+                                                 dims->dtype, span_hint, (hipStream_t)stream, pg));
 }
 
 int attn_update_centroids(const attn_dims* dims, const void* k, const int32_t* seq_lens,
@@ -229,7 +304,7 @@ static int art_common(const attn_dims* dims, const void* q, const void* k, const
                       const int32_t* seq_lens, const int32_t* order, int32_t order_stride,
                       const int32_t* n_visit, float tau, float phi, int32_t patience,
                       int32_t probe_dim, float* out, int32_t* stop_pos, int32_t* blocks_fetched,
-                      void* stream) {
+                      void* stream, const attn_paged_kv* kv = nullptr) {
   int st = check_dims(dims);
   if (st) return st;
   if (!q || !k || !v || !out || !stop_pos) return ATTN_ERR_INVALID_ARG;
@@ -259,7 +334,22 @@ static int art_common(const attn_dims* dims, const void* q, const void* k, const
   a.NBmax = dims->max_blocks;
   a.dtype = dims->dtype;
   a.scale = dims->scale;
+  if (kv) {
+    a.table = kv->block_table;
+    a.table_stride = kv->table_stride;
+    a.pool_blocks = kv->pool_blocks;
+  }
   return hip_status(skv::launch_art(a, (hipStream_t)stream));
+}
+
+int attn_decode_art_paged(const attn_dims* dims, const void* q, const attn_paged_kv* kv, const int32_t* seq_lens,
+                          const int32_t* order, float tau, float phi, int32_t patience, int32_t probe_dim,
+                          float* out, int32_t* stop_pos, int32_t* blocks_fetched, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_paged(dims, kv, true))) return st;
+  return art_common(dims, q, kv->k_pool, kv->v_pool, seq_lens, order, dims->max_blocks, nullptr, tau, phi,
+                    patience, probe_dim, out, stop_pos, blocks_fetched, stream, kv);
 }
 
 int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const void* v,

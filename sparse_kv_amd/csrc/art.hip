@@ -74,9 +74,10 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
   const int lane = threadIdx.x & 63;
   const int NBmax = p.NBmax;
 
-  const size_t slice = (size_t)NBmax * kBlock * ROWB;
-  const auto krs = make_rsrc((const char*)p.k + unit * slice, (uint32_t)L * ROWB);
-  const auto vrs = make_rsrc((const char*)p.v + unit * slice, (uint32_t)L * ROWB);
+  const bool paged = p.table != nullptr;
+  const size_t slice = paged ? 0 : (size_t)NBmax * kBlock * ROWB;
+  auto krs = make_rsrc((const char*)p.k + unit * slice, (uint32_t)L * ROWB);
+  auto vrs = make_rsrc((const char*)p.v + unit * slice, (uint32_t)L * ROWB);
   const int arow = lane & 15, kg = lane >> 4;
   const int aq = 4 * (arow & 3) + (arow >> 2);
   const bool aq_ok = aq < G;
@@ -93,10 +94,11 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
   const int phase = lane / CPR;
   float* pl = sh.p_lds[pi];
 
-  // visit position -> block.  An explicit order's entry for the next position
-  // is read one block ahead, behind that block's K/V loads, so waiting for it
-  // never waits for loads still in flight.
-  auto order_at = [&](int t) { return (p.order && t < nv) ? p.order[(size_t)unit * p.order_stride + t] : 0; };
+  // visit position -> block; explicit order entries come through the scalar
+  // cache, one block ahead
+  auto order_at = [&](int t) {
+    return (p.order && t < nv) ? uniform_load(p.order, (int64_t)unit * p.order_stride + t) : 0;
+  };
   auto block_from = [&](int t, int o) { return p.order ? clampi(o, 0, nb - 1) : (t == 0 ? 0 : nb - t); };
   // read-ahead window: position t may start once t - kR has been folded
   auto window_open = [&](int t) { return ld_acq(&sh.folded) > t - kR; };
@@ -118,8 +120,18 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
 #pragma unroll
     for (int i = 0; i < CPR; ++i) vr[i] = load16_nt(vrs, soff + vvo + i * TPI * ROWB, 0);
   };
+  // byte offset of block j in krs / vrs; a paged cache points them at the
+  // block's own pool run (valid tokens only) and uses offset 0
   auto block_off = [&](int j) {
     if (lane == 0) atomicAdd(&sh.fetched, 1);
+    if (paged) {
+      const int ph = clampi(uniform_load(p.table, (int64_t)b * p.table_stride + j), 0, (int)(p.pool_blocks - 1));
+      const size_t off = ((size_t)ph * p.Hkv + g) * (kBlock * ROWB);
+      const uint32_t n = (uint32_t)min(kBlock, L - j * kBlock) * ROWB;
+      krs = make_rsrc((const char*)p.k + off, n);
+      vrs = make_rsrc((const char*)p.v + off, n);
+      return 0u;
+    }
     return (uint32_t)j * kBlock * ROWB;
   };
 
@@ -133,7 +145,7 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
   }
   while (true) {
     const int tn = t + kNP;
-    int onext = order_at(tn);
+    const int onext = order_at(tn);
     f32x4 sc[4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
@@ -230,7 +242,6 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
 
     if (tn >= nv) return;
     if (!window_wait(tn)) return;
-    asm volatile("" : "+v"(onext));  // keeps the wait for it here, after this block's K/V are used
     j = block_from(tn, onext);
     const uint32_t so = block_off(j);
     load_k(so);

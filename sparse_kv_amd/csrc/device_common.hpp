@@ -152,6 +152,15 @@ __device__ __forceinline__ float elem_f32(const T* p, int i) {
     return ((const float*)p)[i];
 }
 
+// Wave-uniform read of data the kernel never writes (block lists, block
+// tables, visit orders) through the scalar cache: it waits on the scalar
+// counter only, never on vector loads in flight.  The index must be
+// wave-uniform.
+__device__ __forceinline__ int32_t uniform_load(const int32_t* p, int64_t i) {
+  typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
+  return ((const_i32_ptr)p)[i];
+}
+
 __host__ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 }  // namespace skv

@@ -19,6 +19,12 @@ struct DecodeArgs {
   float* o;
   int32_t B, Hq, Hkv, d, NBmax, S, block_begin, block_end, dtype;
   float scale;
+  // paged cache: k, v are pools [pool_blocks, Hkv, 64, d] and table[b *
+  // table_stride + j] is the pool block of logical block j (null: k, v are
+  // contiguous [B, Hkv, NBmax * 64, d])
+  const int32_t* table;
+  int32_t table_stride;
+  int64_t pool_blocks;
 };
 
 struct ArtArgs {
@@ -36,17 +42,26 @@ struct ArtArgs {
   int32_t* blocks_fetched;  // may be null
   int32_t B, Hq, Hkv, d, NBmax, dtype;
   float scale;
+  const int32_t* table;  // paged cache, as in DecodeArgs
+  int32_t table_stride;
+  int64_t pool_blocks;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, bool sparse, hipStream_t st);
 hipError_t launch_merge(int32_t rows, int32_t S, int32_t d, const float* m, const float* l,
                         const float* o, float* out, float* m_out, float* l_out, hipStream_t st);
+// Paged K for the centroid kernels: null table = contiguous k.
+struct PagedK {
+  const int32_t* table;
+  int32_t table_stride;
+  int64_t pool_blocks;
+};
 hipError_t launch_build_centroids(const void* k, const int32_t* seq_lens, float* c, int32_t B,
                                   int32_t Hkv, int32_t d, int32_t NBmax, int32_t dtype,
-                                  hipStream_t st);
+                                  hipStream_t st, PagedK pg = PagedK{nullptr, 0, 0});
 hipError_t launch_update_centroids(const void* k, const int32_t* seq_lens, const int32_t* prev_lens, float* c,
                                    int32_t B, int32_t Hkv, int32_t d, int32_t NBmax, int32_t dtype,
-                                   int32_t span_hint, hipStream_t st);
+                                   int32_t span_hint, hipStream_t st, PagedK pg = PagedK{nullptr, 0, 0});
 hipError_t launch_score(const void* q, const float* c, const int32_t* seq_lens, float* scores,
                         int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t NBmax,
                         int32_t dtype, float scale, hipStream_t st);

@@ -15,22 +15,31 @@ namespace skv {
 namespace {
 
 // ---- centroids: one wave per block, row layout, fp32 sums ---------------
-// Centroid of block j of one (b, kv head) unit: the mean of its valid keys,
-// zeros for a block past the sequence's end.
+// Centroid of block j (wave-uniform) of the (b, g) unit: the mean of its
+// valid keys, zeros for a block past the sequence's end.  K is contiguous
+// [B, Hkv, NBmax * 64, d], or a pool of blocks addressed through pg.table.
 template <typename T, int D>
-__device__ void centroid_block(const void* __restrict__ k, float* __restrict__ C, size_t unit, int j, int L,
-                               int32_t NBmax, int lane) {
+__device__ void centroid_block(const void* __restrict__ k, float* __restrict__ C, int b, int g, int32_t Hkv, int j,
+                               int L, int32_t NBmax, int lane, const PagedK& pg) {
   using Gm = Geo<T, D>;
   constexpr int E = Gm::E, CPR = Gm::CPR, TPI = Gm::TPI, ROWB = Gm::ROWB;
   constexpr bool BF = sizeof(T) == 2;
   const int nb = (L + kBlock - 1) / kBlock;
+  const size_t unit = (size_t)b * Hkv + g;
   float* crow = C + (unit * NBmax + j) * D;
   if (j >= nb) {
     for (int i = lane; i < D; i += 64) crow[i] = 0.f;
     return;
   }
-  const auto rs = make_rsrc((const char*)k + unit * (size_t)NBmax * kBlock * ROWB, (uint32_t)L * ROWB);
-  const uint32_t base = (uint32_t)j * kBlock * ROWB + (uint32_t)(lane / CPR) * ROWB + (uint32_t)(lane % CPR) * 16;
+  size_t boff;
+  if (pg.table) {
+    const int ph = clampi(uniform_load(pg.table, (int64_t)b * pg.table_stride + j), 0, (int)(pg.pool_blocks - 1));
+    boff = ((size_t)ph * Hkv + g) * (kBlock * ROWB);
+  } else {
+    boff = (unit * NBmax + j) * (size_t)(kBlock * ROWB);
+  }
+  const auto rs = make_rsrc((const char*)k + boff, (uint32_t)min(kBlock, L - j * kBlock) * ROWB);
+  const uint32_t base = (uint32_t)(lane / CPR) * ROWB + (uint32_t)(lane % CPR) * 16;
   float sum[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) sum[e] = 0.f;
@@ -60,12 +69,12 @@ __device__ void centroid_block(const void* __restrict__ k, float* __restrict__ C
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void centroid_kernel(const void* __restrict__ k, const int32_t* __restrict__ seq_lens,
-                                                       float* __restrict__ C, int32_t Hkv, int32_t NBmax) {
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                       float* __restrict__ C, int32_t Hkv, int32_t NBmax, PagedK pg) {
+  const int j = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (j >= NBmax) return;
   const int g = blockIdx.y, b = blockIdx.z;
   const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
-  centroid_block<T, D>(k, C, (size_t)b * Hkv + g, j, L, NBmax, threadIdx.x & 63);
+  centroid_block<T, D>(k, C, b, g, Hkv, j, L, NBmax, threadIdx.x & 63, pg);
 }
 
 // Refresh after tokens were appended: blocks [min(prev_len, L) / 64, nb) of
@@ -77,7 +86,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void centroid_update_kernel(const void* __restrict__ k,
                                                               const int32_t* __restrict__ seq_lens,
                                                               const int32_t* __restrict__ prev_lens,
-                                                              float* __restrict__ C, int32_t Hkv, int32_t NBmax) {
+                                                              float* __restrict__ C, int32_t Hkv, int32_t NBmax,
+                                                              PagedK pg) {
   const int g = blockIdx.y, b = blockIdx.z;
   const int Lmax = NBmax * kBlock;
   const int L = clampi(seq_lens ? seq_lens[b] : Lmax, 0, Lmax);
@@ -91,9 +101,8 @@ __global__ __launch_bounds__(256) void centroid_update_kernel(const void* __rest
     lo = max(nb - 1, 0);
     hi = nb;
   }
-  const size_t unit = (size_t)b * Hkv + g;
-  for (int j = lo + blockIdx.x * 4 + (threadIdx.x >> 6); j < hi; j += gridDim.x * 4)
-    centroid_block<T, D>(k, C, unit, j, L, NBmax, threadIdx.x & 63);
+  for (int j = lo + blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); j < hi; j += gridDim.x * 4)
+    centroid_block<T, D>(k, C, b, g, Hkv, j, L, NBmax, threadIdx.x & 63, pg);
 }
 
 // ---- scores: 4 waves x 32 centroid rows per workgroup -------------------
@@ -535,39 +544,39 @@ __global__ __launch_bounds__(256) void two_level_kernel(const void* __restrict__
 
 hipError_t launch_build_centroids(const void* k, const int32_t* seq_lens, float* c, int32_t B,
                                   int32_t Hkv, int32_t d, int32_t NBmax, int32_t dtype,
-                                  hipStream_t st) {
+                                  hipStream_t st, PagedK pg) {
   if (B == 0) return hipSuccess;
   const dim3 grid((NBmax + 3) / 4, Hkv, B);
   if (dtype == 1) {
     if (d == 128)
-      centroid_kernel<__bf16, 128><<<grid, 256, 0, st>>>(k, seq_lens, c, Hkv, NBmax);
+      centroid_kernel<__bf16, 128><<<grid, 256, 0, st>>>(k, seq_lens, c, Hkv, NBmax, pg);
     else
-      centroid_kernel<__bf16, 64><<<grid, 256, 0, st>>>(k, seq_lens, c, Hkv, NBmax);
+      centroid_kernel<__bf16, 64><<<grid, 256, 0, st>>>(k, seq_lens, c, Hkv, NBmax, pg);
   } else {
     if (d == 128)
-      centroid_kernel<float, 128><<<grid, 256, 0, st>>>(k, seq_lens, c, Hkv, NBmax);
+      centroid_kernel<float, 128><<<grid, 256, 0, st>>>(k, seq_lens, c, Hkv, NBmax, pg);
     else
-      centroid_kernel<float, 64><<<grid, 256, 0, st>>>(k, seq_lens, c, Hkv, NBmax);
+      centroid_kernel<float, 64><<<grid, 256, 0, st>>>(k, seq_lens, c, Hkv, NBmax, pg);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_update_centroids(const void* k, const int32_t* seq_lens, const int32_t* prev_lens, float* c,
                                    int32_t B, int32_t Hkv, int32_t d, int32_t NBmax, int32_t dtype,
-                                   int32_t span_hint, hipStream_t st) {
+                                   int32_t span_hint, hipStream_t st, PagedK pg) {
   if (B == 0) return hipSuccess;
   const int X = clampi((span_hint + 3) / 4, 1, (NBmax + 3) / 4);
   const dim3 grid(X, Hkv, B);
   if (dtype == 1) {
     if (d == 128)
-      centroid_update_kernel<__bf16, 128><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax);
+      centroid_update_kernel<__bf16, 128><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax, pg);
     else
-      centroid_update_kernel<__bf16, 64><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax);
+      centroid_update_kernel<__bf16, 64><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax, pg);
   } else {
     if (d == 128)
-      centroid_update_kernel<float, 128><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax);
+      centroid_update_kernel<float, 128><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax, pg);
     else
-      centroid_update_kernel<float, 64><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax);
+      centroid_update_kernel<float, 64><<<grid, 256, 0, st>>>(k, seq_lens, prev_lens, c, Hkv, NBmax, pg);
   }
   return hipGetLastError();
 }

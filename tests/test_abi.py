@@ -111,6 +111,30 @@ def test_argument_validation(skv):
     assert tl(dims(max_blocks=4097 * 2), 2, 1, 1, 4) == -2  # more than 4096 super-blocks
     assert tl(dims(max_blocks=16384), 16, 513, 1, 4) == -2  # 513 * 16 candidates
     assert tl(dims(batch=0, max_blocks=8192), 16, 512, 1, 4) == 0
+    # paged cache descriptors: pools, a table of >= max_blocks entries per row, pool_blocks >= 1
+    from sparse_kv_amd import AttnPagedKV
+
+    good = AttnPagedKV(0x1000, 0x1000, 16, 0x1000, 4)
+    for bad in (AttnPagedKV(None, 0x1000, 16, 0x1000, 4), AttnPagedKV(0x1000, None, 16, 0x1000, 4),
+                AttnPagedKV(0x1000, 0x1000, 0, 0x1000, 4), AttnPagedKV(0x1000, 0x1000, 16, None, 4),
+                AttnPagedKV(0x1000, 0x1000, 16, 0x1000, 3)):
+        assert lib.attn_decode_dense_paged(ctypes.byref(d), FAKE, ctypes.byref(bad), None, 0, -1, 4, FAKE, FAKE, FAKE,
+                                           None) == -1
+    assert lib.attn_decode_dense_paged(ctypes.byref(d), FAKE, None, None, 0, -1, 4, FAKE, FAKE, FAKE, None) == -1
+    assert lib.attn_decode_dense_paged(ctypes.byref(d), FAKE, ctypes.byref(good), None, 0, -1, 0, FAKE, FAKE, FAKE,
+                                       None) == -1
+    assert lib.attn_decode_sparse_paged(ctypes.byref(d), FAKE, ctypes.byref(good), None, None, FAKE, 4, 2, FAKE, FAKE,
+                                        FAKE, None) == -1
+    konly = AttnPagedKV(0x1000, None, 16, 0x1000, 4)  # centroids read K only
+    assert lib.attn_build_centroids_paged(ctypes.byref(d), ctypes.byref(konly), None, None, None) == -1
+    assert lib.attn_update_centroids_paged(ctypes.byref(d), ctypes.byref(konly), None, None, 0, FAKE, None) == -1
+    assert lib.attn_decode_art_paged(ctypes.byref(d), FAKE, ctypes.byref(konly), None, None, 1e-3, 1e-4, 2, 8, FAKE,
+                                     FAKE, None, None) == -1
+    assert lib.attn_decode_art_paged(ctypes.byref(d), FAKE, ctypes.byref(good), None, None, 1e-3, 1e-4, 0, 8, FAKE,
+                                     FAKE, None, None) == -1
+    d0 = dims(batch=0)
+    assert lib.attn_decode_dense_paged(ctypes.byref(d0), FAKE, ctypes.byref(good), None, 0, -1, 4, FAKE, FAKE, FAKE,
+                                       None) == 0
     # importance order: scores and order are required; at most 16384 blocks after the sink
     assert lib.attn_order_blocks(ctypes.byref(d), None, None, FAKE, None) == -1
     assert lib.attn_order_blocks(ctypes.byref(d), FAKE, None, None, None) == -1

@@ -281,3 +281,46 @@ def test_two_level_selection_exact(label, group, kc, k, ns, nr, seq):
         one = skv.attn_select_topk(skv.attn_score_centroids(q, C, sl), sl, k=k, n_sink_blocks=ns, n_recent_blocks=nr)
         torch.cuda.synchronize()
         assert np.array_equal(one[0].cpu().numpy(), idx) and np.array_equal(one[1].cpu().numpy(), n)
+
+
+def test_decoupled_forecast_selection():
+    """Selection driven by a per-KV-head forecast vector that is not the
+    attention query (one forecast head per GQA group); attention then runs
+    with the real queries over the forecast's blocks."""
+    import sparse_kv_amd as skv
+    from tests.gpu_util import to_dev
+
+    log("[select] decoupled forecast query")
+    B, Hq, Hkv, d, L = 2, 8, 2, 128, 64 * 40
+    k_top, ns, nr = 6, 1, 3
+    attempts = {}
+    for _ in range(30):
+        inp = synth.make_inputs(35, B, Hq, Hkv, d, L, kind="mixture", seq_lens=[64 * 40, 64 * 27 + 11],
+                                attempts=attempts)
+        fc = synth.round_to_bf16(np.random.default_rng(3500 + sum(attempts.values())).standard_normal(
+            (B, Hkv, d)).astype(np.float32))
+        qf, kf, vf = inp.f64()
+        ff = synth.bf16_to_f32(fc).astype(np.float64)
+        sig = oracle.centroid_scores(ff, oracle.block_centroids(kf, inp.seq_lens), inp.seq_lens, inp.scale)
+        bad = [(b, g) for b in range(B) for g in range(Hkv)
+               if selection_gap(sig[b, g], -(-int(inp.seq_lens[b]) // 64), k_top, ns, nr) <= 1e-4]
+        if not bad:
+            break
+        for u in bad:
+            attempts[u] = attempts.get(u, 0) + 1
+    else:
+        raise AssertionError("no margin")
+    lists = oracle.select_all(sig, inp.seq_lens, k_top, ns, nr)
+    q, k, v, sl = upload(inp)
+    f = to_dev(fc, "bf16")
+    C = skv.attn_build_centroids(k, sl)
+    idx, n = skv.attn_select_topk(skv.attn_score_centroids(f, C, sl, scale=inp.scale), sl, k=k_top,
+                                  n_sink_blocks=ns, n_recent_blocks=nr)
+    out = skv.attn_merge_states(*skv.attn_decode_sparse(q, k, v, idx, n, sl, num_splits=3))
+    torch.cuda.synchronize()
+    idx, n = idx.cpu().numpy(), n.cpu().numpy()
+    for b in range(B):
+        for g in range(Hkv):
+            assert idx[b, g, :n[b, g]].tolist() == lists[b][g]
+    assert_close(out.cpu().numpy(), oracle.decode_blocks(qf, kf, vf, inp.seq_lens, inp.scale, lists), TOL,
+                 "attention over the forecast's blocks")
