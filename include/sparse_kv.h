@@ -40,6 +40,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbol visibility; the declarations below
+ * are its whole exported interface. */
+#pragma GCC visibility push(default)
+
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = -1, /* a NULL required pointer, a bad size or dim      */
@@ -348,6 +352,8 @@ size_t attn_routed_workspace_bytes(const attn_dims* dims, int32_t n_shards,
 
 /* Static description of a status code (never NULL). */
 const char* attn_status_string(int status);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of the generated code on purpose.
 CFLAGS = [
-    "-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-Wall",
+    "-O3", f"--offload-arch={ARCH}", "-fPIC", "-fvisibility=hidden", "-std=c++17", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INC, "-I", SRC,
 ]
