@@ -42,12 +42,19 @@ __device__ __forceinline__ void st_rel(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// NP producer waves, R ring slots (R also bounds the read-ahead).
+// NP producer waves, R ring slots (R also bounds the read-ahead).  Each
+// producer has a scratch area: its block's K rows (KROWS, padded by 16 bytes
+// per row so the MFMA-layout reads are free of bank conflicts), then the
+// block's softmax weights, which reuse the space once the logits are formed.
 template <typename T, int D, int GR, int NP, int R>
 struct ArtShared {
   static constexpr int GP = 4 * GR;
   static constexpr int kNP = NP, kR = R;
-  float p_lds[NP][64 * GP];
+  static constexpr int kRowB = D * (int)sizeof(T);
+  static constexpr bool kKRows = GR == 1 && kRowB <= 256;
+  static constexpr int kKStride = kRowB + 16;
+  static constexpr int kScratch = kKRows ? 64 * kKStride : 64 * GP * 4;
+  __attribute__((aligned(16))) char scratch[NP][kScratch];
   float slot_acc[R][GP][D];
   float slot_m[R][GP];
   float slot_l[R][GP];
@@ -60,9 +67,13 @@ struct ArtShared {
 };
 
 // Producer wave pi: visit positions pi, pi + NP, ...  Each block is loaded
-// whole (K in the MFMA operand layout, V in the row layout) before its
-// logits, softmax and P.V; with NP producers per workgroup, NP blocks are in
-// flight per CU.
+// whole before its logits, softmax and P.V; with NP producers per
+// workgroup, NP blocks are in flight per CU.  V is read in the row layout
+// (whole 128-byte lines per instruction, non-temporal).  K is read the same
+// way when SH::kKRows and moved into the MFMA operand layout through LDS:
+// the operand layout read straight from memory touches half of 16 lines
+// per instruction, which a CU streams about 30% slower than whole lines --
+// and with fewer units than CUs each unit runs at its CU's read limit.
 template <typename T, int D, int GR, typename SH>
 __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, int g, int G, int L, int nb,
                              int nv) {
@@ -92,7 +103,10 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
   const uint32_t kvo = (uint32_t)arow * ROWB + (uint32_t)kg * 16;
   const uint32_t vvo = (uint32_t)(lane / CPR) * ROWB + (uint32_t)(lane % CPR) * 16;
   const int phase = lane / CPR;
-  float* pl = sh.p_lds[pi];
+  char* scr = sh.scratch[pi];
+  float* pl = (float*)scr;
+  constexpr bool KROWS = SH::kKRows;
+  constexpr int KSTR = SH::kKStride;
 
   // visit position -> block; explicit order entries come through the scalar
   // cache, one block ahead
@@ -110,11 +124,31 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
     }
   };
   u32x4 kr[4][KA], vr[CPR];
+  u32x4 kraw[KROWS ? CPR : 1];
   auto load_k = [&](uint32_t soff) {
+    if constexpr (KROWS) {
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
+      for (int i = 0; i < CPR; ++i) kraw[i] = load16_nt(krs, soff + vvo + i * TPI * ROWB, 0);
+    } else {
 #pragma unroll
-      for (int a = 0; a < KA; ++a) kr[t4][a] = load16(krs, soff + kvo + t4 * 16 * ROWB + a * 64, 0);
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int a = 0; a < KA; ++a) kr[t4][a] = load16(krs, soff + kvo + t4 * 16 * ROWB + a * 64, 0);
+    }
+  };
+  // K rows -> MFMA operand layout (row 16 t4 + arow, 16-byte chunk 4 a + kg)
+  auto k_to_operands = [&]() {
+    if constexpr (KROWS) {
+#pragma unroll
+      for (int i = 0; i < CPR; ++i)
+        *(u32x4*)(scr + (i * TPI + phase) * KSTR + (lane % CPR) * 16) = kraw[i];
+      wave_lds_exchange();
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int a = 0; a < KA; ++a) kr[t4][a] = *(const u32x4*)(scr + (16 * t4 + arow) * KSTR + (4 * a + kg) * 16);
+      wave_lds_exchange();  // the weight table reuses the space
+    }
   };
   auto load_v = [&](uint32_t soff) {
 #pragma unroll
@@ -146,6 +180,7 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
   while (true) {
     const int tn = t + kNP;
     const int onext = order_at(tn);
+    k_to_operands();
     f32x4 sc[4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
