@@ -70,7 +70,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--splits", type=int, default=16, help="splits per (batch row, KV head), dense stage")
+    ap.add_argument("--splits", type=int, default=4,
+                    help="splits per (batch row, KV head), dense stage (4: one workgroup per CU at batch 8)")
     ap.add_argument("--sparse-splits", type=int, default=4, help="splits per unit, sparse stage")
     ap.add_argument("--window-splits", type=int, default=4, help="splits per unit, sink+window stage")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
@@ -426,7 +427,8 @@ def bench_art64k(args):
     del inp
     out, stop, fetched = skv.attn_decode_art(q, k, v, None, tau=W["tau"], phi=W["phi"], patience=W["patience"],
                                              probe_dim=W["probe_dim"])
-    m, l, o = skv.attn_decode_dense(q, k, v, None, num_splits=16)
+    S = max(1, 256 // (B * Hkv))  # one workgroup per CU
+    m, l, o = skv.attn_decode_dense(q, k, v, None, num_splits=S)
     od = skv.attn_merge_states(m, l, o)
     ta, td, t0, toff = _timer(), _timer(), _timer(), _timer()
     for i in range(args.warmup + args.steps):
@@ -435,7 +437,7 @@ def bench_art64k(args):
             skv.attn_decode_art(q, k, v, None, tau=W["tau"], phi=W["phi"], patience=W["patience"],
                                 probe_dim=W["probe_dim"], out=out, stop_pos=stop, blocks_fetched=fetched)
         with (td if rec else _timer()):
-            skv.attn_decode_dense(q, k, v, None, num_splits=16, m=m, l=l, o=o)
+            skv.attn_decode_dense(q, k, v, None, num_splits=S, m=m, l=l, o=o)
             skv.attn_merge_states(m, l, o, out=od)
     for i in range(3):  # detector overhead: no early exit (tau = phi = 0) vs detector off
         with t0:

@@ -22,8 +22,11 @@
 //     lane/CPR = token phase; one wave-wide load covers whole rows), where
 //     P.V is accumulated in fp32 with VALU FMAs: P is never rounded to bf16.
 //   * V is read with streaming (non-temporal) loads, whole rows per
-//     instruction; K, whose MFMA layout covers half a 128-byte line per
-//     instruction, goes through L2 so the second half is an L2 hit.
+//     instruction.  K is read the same way when a padded 64-row tile per
+//     wave fits in LDS (G <= 4 and rows of at most 256 bytes) and moved into
+//     the MFMA operand layout there; otherwise it is read straight into that
+//     layout, half a 128-byte line per instruction, through L2 so that the
+//     second half is an L2 hit.
 //   * Reads past the sequence end hit the buffer range limit and return
 //     zeros (the whole byte offset goes in the VGPR offset, which is what the
 //     range check covers); their logits are masked to -inf.
@@ -51,7 +54,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   constexpr int E = Gm::E, CPR = Gm::CPR, TPI = Gm::TPI, KA = Gm::KA, ROWB = Gm::ROWB;
   constexpr bool BF = sizeof(T) == 2;
 
-  __shared__ float p_lds[kWaves][64 * GP];
+  // per-wave scratch: the block's K rows (KROWS; 16 bytes of padding per row
+  // keep the operand-layout reads free of bank conflicts), then its softmax
+  // weights, which reuse the space once the logits are formed
+  constexpr bool KROWS = GR == 1 && ROWB <= 256;
+  constexpr int KSTR = ROWB + 16;
+  constexpr int SCR = KROWS ? 64 * KSTR : 64 * GP * 4;
+  __shared__ __attribute__((aligned(16))) char scratch[kWaves][SCR];
   __shared__ float red_acc[kWaves][GP][D];
   __shared__ float red_m[kWaves][GP];
   __shared__ float red_l[kWaves][GP];
@@ -115,7 +124,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[q][e] = 0.f;
 
-  float* pl = p_lds[w];
+  char* scr = scratch[w];
+  float* pl = (float*)scr;
   const int32_t* list = SPARSE ? p.block_idx + unit * (size_t)p.max_sel : nullptr;
 
   // Software pipeline: the next block's K is requested as soon as this
@@ -123,6 +133,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   // every wave keeps a block's worth of loads in flight while it computes.
   u32x4 kr[4][KA];
   u32x4 vr[CPR];
+  u32x4 kraw[KROWS ? CPR : 1];
   auto block_at = [&](int pos) { return SPARSE ? clampi(uniform_load(list, pos), 0, nb - 1) : pos; };
   auto load_k = [&](int j) {
     auto rs = krs;
@@ -131,10 +142,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
       rs = make_rsrc((const char*)p.k + pool_off(j), valid_bytes(j));
       soff = 0;
     }
+    if constexpr (KROWS) {
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
+      for (int i = 0; i < CPR; ++i) kraw[i] = load16_nt(rs, soff + vvo + i * TPI * ROWB, 0);
+    } else {
 #pragma unroll
-      for (int a = 0; a < KA; ++a) kr[t4][a] = load16(rs, soff + kvo + t4 * 16 * ROWB + a * 64, 0);
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int a = 0; a < KA; ++a) kr[t4][a] = load16(rs, soff + kvo + t4 * 16 * ROWB + a * 64, 0);
+    }
+  };
+  // K rows -> MFMA operand layout (row 16 t4 + arow, 16-byte chunk 4 a + kg)
+  auto k_to_operands = [&]() {
+    if constexpr (KROWS) {
+#pragma unroll
+      for (int i = 0; i < CPR; ++i)
+        *(u32x4*)(scr + (i * TPI + lane / CPR) * KSTR + (lane % CPR) * 16) = kraw[i];
+      wave_lds_exchange();
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int a = 0; a < KA; ++a) kr[t4][a] = *(const u32x4*)(scr + (16 * t4 + arow) * KSTR + (4 * a + kg) * 16);
+      wave_lds_exchange();  // the weight table reuses the space
+    }
   };
   auto load_v = [&](int j) {
     auto rs = vrs;
@@ -156,6 +186,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
   for (int pos = lo + w; pos < hi; pos += kWaves) {
     const int j = jn;
     const bool more = pos + kWaves < hi;
+    k_to_operands();
 
     // logits: sc[t4][r] = <q_{4r + kg}, k_{16 t4 + arow}>
     f32x4 sc[4];
