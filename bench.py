@@ -43,9 +43,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_decode128k_b8.md")
 DENSE_SOURCES = ("decode.hip", "device_common.hpp", "kernels.hpp")
 
 
-def measured_dense_traffic():
+def measured_dense_traffic(splits):
     """HBM bytes per dense-kernel launch from the committed counter summary,
-    or None when the kernel sources changed since the counters were taken."""
+    or None when the kernel sources changed since the counters were taken or
+    the launch uses another split count."""
     import hashlib
 
     try:
@@ -59,6 +60,8 @@ def measured_dense_traffic():
             with open(os.path.join(ROOT, "sparse_kv_amd", "csrc", f), "rb") as fh:
                 h.update(fh.read())
         if h.hexdigest() != kv.get("dense_decode_source_sha256"):
+            return None
+        if int(kv.get("dense_decode_splits", -1)) != splits:
             return None
         return int(kv["dense_decode_traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -370,7 +373,7 @@ def main():
         ach = kb / (paths["dense"]["kernel_ms"] * 1e-3) / 1e9
         res["roofline"] = {"kernel": "decode_kernel (split-KV dense)", "bound": "hbm", "achieved": round(ach, 1),
                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                           "traffic": measured_dense_traffic(), "bytes_per_launch": kb,
+                           "traffic": measured_dense_traffic(S), "bytes_per_launch": kb,
                            "avg_launch_ms": round(paths["dense"]["kernel_ms"], 5)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, topk, n_sink, n_recent, win_recent,

@@ -396,8 +396,9 @@ int attn_decode_routed(const attn_dims* dims, int32_t n_layers, const uint8_t* r
   int st = check_dims(dims);
   if (st) return st;
   if (n_layers < 0 || !route_mask || !q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
-  if (n_shards < 1 || splits_per_shard < 1 || sa_splits < 1) return ATTN_ERR_INVALID_ARG;
+  if (n_shards < 1 || splits_per_shard < 1 || sa_splits < 1 || sa_splits > (1 << 24)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)n_shards * splits_per_shard > (1 << 24)) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)dims->batch * dims->num_q_heads * n_shards > 0x7fffffff) return ATTN_ERR_INVALID_ARG;
   bool any_sa = false;
   for (int32_t i = 0; i < n_layers; ++i) {
     if (!q[i] || !k[i] || !v[i] || !out[i]) return ATTN_ERR_INVALID_ARG;

@@ -161,6 +161,10 @@ def test_routed_workspace_and_validation(skv):
         None, 8, 2, sa, FAKE, 4, 4, FAKE, ws_bytes, ctypes.cast(ptrs, P), None)
     assert call(small - 1) == -4
     assert call(small, sa=None) == -1  # a sparse layer needs its block list
+    big_sa = lib.attn_decode_routed(ctypes.byref(d), 2, ctypes.cast(mask, P), ctypes.cast(ptrs, P),
+                                    ctypes.cast(ptrs, P), ctypes.cast(ptrs, P), None, 8, 2, FAKE, FAKE, 4,
+                                    (1 << 24) + 1, FAKE, 1 << 40, ctypes.cast(ptrs, P), None)
+    assert big_sa == -1  # split counts are bounded
 
 
 def test_status_strings(skv):
