@@ -181,164 +181,6 @@ __device__ int block_exscan(int x, int* total, int* lds4) {
   return base + inc - x;
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
-                                                   int32_t Hkv, int32_t NBmax, int32_t k, int32_t n_sink,
-                                                   int32_t n_recent, int32_t max_sel, int32_t* __restrict__ idx,
-                                                   int32_t* __restrict__ n_sel) {
-  __shared__ uint32_t hist[256];
-  __shared__ int scan4[4];
-  __shared__ uint32_t sh_prefix;
-  __shared__ int sh_rem;
-  const int unit = blockIdx.x, b = unit / Hkv, tid = threadIdx.x;
-  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
-  const int nb = (L + kBlock - 1) / kBlock;
-  const float* row = scores + (size_t)unit * NBmax;
-  int32_t* out = idx + (size_t)unit * max_sel;
-
-  // forced blocks: [0, sink_hi) and [rec_lo, nb); candidates: [sink_hi, rec_lo)
-  const int sink_hi = min(n_sink, nb);
-  const int rec_lo = max(nb - n_recent, sink_hi);
-  const int ncand = rec_lo - sink_hi;
-  const int kk = min(k, ncand);
-  const bool take_all = kk == ncand;
-  const bool ranked = kk > 0 && !take_all;
-
-  // radix select of the kk-th largest key, 8 bits per pass
-  uint32_t thr = 0;
-  int need_eq = 0;
-  if (ranked) {
-    uint32_t prefix = 0, mask = 0;
-    int rem = kk;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      hist[tid] = 0;
-      __syncthreads();
-      for (int j = sink_hi + tid; j < rec_lo; j += 256) {
-        const uint32_t u = score_key(row[j]);
-        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      const int bin = 255 - tid;  // thread 0 takes the highest digit
-      const int x = (int)hist[bin];
-      int tot;
-      const int above = block_exscan(x, &tot, scan4);
-      if (above < rem && rem <= above + x) {
-        sh_prefix = prefix | ((uint32_t)bin << shift);
-        sh_rem = rem - above;
-      }
-      __syncthreads();
-      prefix = sh_prefix;
-      rem = sh_rem;
-      mask |= 255u << shift;
-      __syncthreads();
-    }
-    thr = prefix;
-    need_eq = rem;  // keys equal to thr still to take, lowest index first
-  }
-
-  // each thread owns a contiguous chunk so that scans follow index order
-  const int CH = (nb + 255) / 256;
-  const int j0 = min(tid * CH, nb), j1 = min(j0 + CH, nb);
-  int eq_local = 0;
-  if (ranked)
-    for (int j = j0; j < j1; ++j)
-      if (j >= sink_hi && j < rec_lo && score_key(row[j]) == thr) ++eq_local;
-  int tot_eq;
-  const int eq_before = block_exscan(eq_local, &tot_eq, scan4);
-
-  auto chosen = [&](int j, int& eq_seen) -> bool {
-    if (j < sink_hi || j >= rec_lo) return true;
-    if (kk == 0) return false;
-    if (take_all) return true;
-    const uint32_t u = score_key(row[j]);
-    if (u > thr) return true;
-    if (u == thr) return eq_seen++ < need_eq;
-    return false;
-  };
-  int eq_seen = eq_before, cnt = 0;
-  for (int j = j0; j < j1; ++j) cnt += chosen(j, eq_seen) ? 1 : 0;
-  int total;
-  int pos = block_exscan(cnt, &total, scan4);
-  eq_seen = eq_before;
-  for (int j = j0; j < j1; ++j)
-    if (chosen(j, eq_seen) && pos < max_sel) out[pos++] = j;
-  for (int i = total + tid; i < max_sel; i += 256) out[i] = -1;
-  if (tid == 0) n_sel[unit] = min(total, max_sel);
-}
-
-// ---- importance order: one workgroup per (b, kv head) -------------------
-// Block 0 first, then blocks 1 .. nb-1 by descending score, lower index first
-// among equal scores ("ART" summary, §2.4, importance-first visit order).
-// The nb - 1 keys (inverted score key << 32 | block) are sorted ascending by
-// a bitonic network in LDS, padded to a power of two with all-ones keys.
-template <int CAP>
-__global__ __launch_bounds__(1024) void order_kernel(const float* __restrict__ scores,
-                                                     const int32_t* __restrict__ seq_lens, int32_t Hkv,
-                                                     int32_t NBmax, int32_t* __restrict__ order) {
-  __shared__ uint64_t key[CAP];
-  const int unit = blockIdx.x, b = unit / Hkv, tid = threadIdx.x;
-  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
-  const int nb = (L + kBlock - 1) / kBlock;
-  const float* row = scores + (size_t)unit * NBmax;
-  int32_t* out = order + (size_t)unit * NBmax;
-  const int nr = max(nb - 1, 0);  // blocks after the sink
-  int n = 2;
-  while (n < nr) n <<= 1;
-  for (int i = tid; i < n; i += 1024)
-    key[i] = i < nr ? ((uint64_t)~score_key(row[i + 1]) << 32) | (uint32_t)(i + 1) : ~(uint64_t)0;
-  __syncthreads();
-  for (int kk = 2; kk <= n; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int pr = tid; pr < (n >> 1); pr += 1024) {
-        const int i = 2 * j * (pr / j) + pr % j;  // pair (i, i + j)
-        const uint64_t x = key[i], y = key[i + j];
-        const bool up = (i & kk) == 0;
-        if ((x > y) == up) {
-          key[i] = y;
-          key[i + j] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = tid; i < NBmax; i += 1024)
-    out[i] = i == 0 ? (nb > 0 ? 0 : -1) : (i < nb ? (int32_t)(uint32_t)key[i - 1] : -1);
-}
-
-// ---- two-level selection ---------------------------------------------------
-// Super-block centroids from block centroids: the token-count-weighted mean
-// of the block means is the mean of the super-block's keys.
-template <int D>
-__global__ __launch_bounds__(256) void super_centroid_kernel(const float* __restrict__ C,
-                                                             const int32_t* __restrict__ seq_lens,
-                                                             float* __restrict__ C2, int32_t Hkv, int32_t NBmax,
-                                                             int32_t NSmax, int32_t group) {
-  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (s >= NSmax) return;
-  const int g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
-  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
-  const int nb = (L + kBlock - 1) / kBlock;
-  const size_t unit = (size_t)b * Hkv + g;
-  float* out = C2 + (unit * NSmax + s) * D;
-  const int j0 = s * group, j1 = min(j0 + group, nb);
-  if (j0 >= j1) {
-    for (int c = lane; c < D; c += 64) out[c] = 0.f;
-    return;
-  }
-  const float* crow = C + (unit * NBmax) * D;
-  float acc[D / 64];
-#pragma unroll
-  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-  for (int j = j0; j < j1; ++j) {
-    const float nj = (float)min(kBlock, L - j * kBlock);
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) acc[e] = fmaf(nj, crow[(size_t)j * D + lane + 64 * e], acc[e]);
-  }
-  const float n = (float)(min(L, j1 * kBlock) - j0 * kBlock);
-#pragma unroll
-  for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = acc[e] / n;
-}
-
 // Radix select (8 bits a pass, 256-thread workgroup) of the kk-th largest
 // key among items [0, n) with elig(i): returns that key and how many items
 // equal to it are to be taken (lowest indices first).  0 < kk < #eligible.
@@ -418,6 +260,125 @@ __device__ int take_best(int n, int kk, KeyF key, EligF elig, TakeF take, uint32
     if (chosen(i, eq_seen)) take(i, rank++);
   __syncthreads();
   return total;
+}
+
+// The candidates' order-preserving keys are staged in LDS once (rows of up
+// to kTopkStage candidates; longer rows are read from memory in every pass),
+// then take_best's radix select and index-ordered compaction pick the k.
+constexpr int kTopkStage = 16384;
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
+                                                   int32_t Hkv, int32_t NBmax, int32_t k, int32_t n_sink,
+                                                   int32_t n_recent, int32_t max_sel, int32_t* __restrict__ idx,
+                                                   int32_t* __restrict__ n_sel) {
+  __shared__ uint32_t keys[kTopkStage];
+  __shared__ uint32_t hist[256];
+  __shared__ int scan4[4];
+  __shared__ uint32_t sh_prefix;
+  __shared__ int sh_rem;
+  const int unit = blockIdx.x, b = unit / Hkv, tid = threadIdx.x;
+  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
+  const int nb = (L + kBlock - 1) / kBlock;
+  const float* row = scores + (size_t)unit * NBmax;
+  int32_t* out = idx + (size_t)unit * max_sel;
+
+  // forced blocks: [0, sink_hi) and [rec_lo, nb); candidates: [sink_hi, rec_lo)
+  const int sink_hi = min(n_sink, nb);
+  const int rec_lo = max(nb - n_recent, sink_hi);
+  const int ncand = rec_lo - sink_hi;
+  const bool staged = ncand <= kTopkStage;
+  if (staged && k > 0)  // with k = 0 no score is read (scores may be null)
+    for (int i = tid; i < ncand; i += 256) keys[i] = score_key(row[sink_hi + i]);
+  __syncthreads();
+  auto key = [&](int i) { return staged ? keys[i] : score_key(row[sink_hi + i]); };
+  const int npick = take_best(
+      ncand, k, key, [](int) { return true; },
+      [&](int i, int r) {
+        if (sink_hi + r < max_sel) out[sink_hi + r] = sink_hi + i;
+      },
+      hist, scan4, &sh_prefix, &sh_rem);
+  for (int j = tid; j < sink_hi; j += 256)
+    if (j < max_sel) out[j] = j;
+  for (int j = rec_lo + tid; j < nb; j += 256) {
+    const int o = sink_hi + npick + (j - rec_lo);
+    if (o < max_sel) out[o] = j;
+  }
+  const int total = sink_hi + npick + (nb - rec_lo);
+  for (int o = total + tid; o < max_sel; o += 256) out[o] = -1;
+  if (tid == 0) n_sel[unit] = min(total, max_sel);
+}
+
+// ---- importance order: one workgroup per (b, kv head) -------------------
+// Block 0 first, then blocks 1 .. nb-1 by descending score, lower index first
+// among equal scores ("ART" summary, §2.4, importance-first visit order).
+// The nb - 1 keys (inverted score key << 32 | block) are sorted ascending by
+// a bitonic network in LDS, padded to a power of two with all-ones keys.
+template <int CAP>
+__global__ __launch_bounds__(1024) void order_kernel(const float* __restrict__ scores,
+                                                     const int32_t* __restrict__ seq_lens, int32_t Hkv,
+                                                     int32_t NBmax, int32_t* __restrict__ order) {
+  __shared__ uint64_t key[CAP];
+  const int unit = blockIdx.x, b = unit / Hkv, tid = threadIdx.x;
+  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
+  const int nb = (L + kBlock - 1) / kBlock;
+  const float* row = scores + (size_t)unit * NBmax;
+  int32_t* out = order + (size_t)unit * NBmax;
+  const int nr = max(nb - 1, 0);  // blocks after the sink
+  int n = 2;
+  while (n < nr) n <<= 1;
+  for (int i = tid; i < n; i += 1024)
+    key[i] = i < nr ? ((uint64_t)~score_key(row[i + 1]) << 32) | (uint32_t)(i + 1) : ~(uint64_t)0;
+  __syncthreads();
+  for (int kk = 2; kk <= n; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int pr = tid; pr < (n >> 1); pr += 1024) {
+        const int i = 2 * j * (pr / j) + pr % j;  // pair (i, i + j)
+        const uint64_t x = key[i], y = key[i + j];
+        const bool up = (i & kk) == 0;
+        if ((x > y) == up) {
+          key[i] = y;
+          key[i + j] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < NBmax; i += 1024)
+    out[i] = i == 0 ? (nb > 0 ? 0 : -1) : (i < nb ? (int32_t)(uint32_t)key[i - 1] : -1);
+}
+
+// ---- two-level selection ---------------------------------------------------
+// Super-block centroids from block centroids: the token-count-weighted mean
+// of the block means is the mean of the super-block's keys.
+template <int D>
+__global__ __launch_bounds__(256) void super_centroid_kernel(const float* __restrict__ C,
+                                                             const int32_t* __restrict__ seq_lens,
+                                                             float* __restrict__ C2, int32_t Hkv, int32_t NBmax,
+                                                             int32_t NSmax, int32_t group) {
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= NSmax) return;
+  const int g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
+  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
+  const int nb = (L + kBlock - 1) / kBlock;
+  const size_t unit = (size_t)b * Hkv + g;
+  float* out = C2 + (unit * NSmax + s) * D;
+  const int j0 = s * group, j1 = min(j0 + group, nb);
+  if (j0 >= j1) {
+    for (int c = lane; c < D; c += 64) out[c] = 0.f;
+    return;
+  }
+  const float* crow = C + (unit * NBmax) * D;
+  float acc[D / 64];
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+  for (int j = j0; j < j1; ++j) {
+    const float nj = (float)min(kBlock, L - j * kBlock);
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) acc[e] = fmaf(nj, crow[(size_t)j * D + lane + 64 * e], acc[e]);
+  }
+  const float n = (float)(min(L, j1 * kBlock) - j0 * kBlock);
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = acc[e] / n;
 }
 
 // Scores n centroid rows against the LDS query qs: 16-byte loads, D/4 lanes
