@@ -65,9 +65,16 @@ def test_sparse_128k_batch8_selection_and_dense():
     C = skv.attn_build_centroids(k)
     sc = skv.attn_score_centroids(q, C)
     idx, n = skv.attn_select_topk(sc, None, k=k_top, n_sink_blocks=ns, n_recent_blocks=nr)
-    sp = skv.attn_merge_states(*skv.attn_decode_sparse(q, k, v, idx, n, None, num_splits=12))
+    sp = skv.attn_merge_states(*skv.attn_decode_sparse(q, k, v, idx, n, None, num_splits=4))  # the benchmark's launch
+    # the sink + window stage: block 0 and the last 128 blocks, 4 splits
+    widx, wn = skv.attn_select_topk(None, None, k=0, n_sink_blocks=1, n_recent_blocks=128, shape=(B, Hkv, L // 64),
+                                    device="cuda")
+    win = skv.attn_merge_states(*skv.attn_decode_sparse(q, k, v, widx, wn, None, num_splits=4))
     torch.cuda.synchronize()
     dense, sp, idx, n = dense.cpu().numpy(), sp.cpu().numpy(), idx.cpu().numpy(), n.cpu().numpy()
+    win = win.cpu().numpy()
+    window = [0] + list(range(L // 64 - 128, L // 64))
+    assert (wn.cpu().numpy() == 129).all() and (widx.cpu().numpy()[:, :, :129] == np.array(window)).all()
     assert (n == ns + nr + k_top).all()
     G = Hq // Hkv
     checked = 0
@@ -85,6 +92,8 @@ def test_sparse_128k_batch8_selection_and_dense():
         got = [[idx[b, g, :n[b, g]].tolist()]]
         ref = oracle.decode_blocks(qf, kf, vf, seq, inp.scale, got)
         assert_close(sp[b, g * G:(g + 1) * G], ref[0], TOL, f"sparse unit ({b},{g})")
+        assert_close(win[b, g * G:(g + 1) * G], oracle.decode_blocks(qf, kf, vf, seq, inp.scale, [[window]])[0], TOL,
+                     f"sink + window unit ({b},{g})")
     assert checked >= 2, "too few sampled units with a clear top-k margin"
 
 
