@@ -170,3 +170,22 @@ def test_routed_workspace_and_validation(skv):
 def test_status_strings(skv):
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(skv.attn_status_string(code), str) and skv.attn_status_string(code)
+
+
+def test_header_is_plain_c_and_links(skv, tmp_path):
+    """include/sparse_kv.h compiles as C99 and a C program linked against the
+    library gets the documented status codes (validation paths only)."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = os.path.join(ROOT, "tests", "c", "abi_from_c.c")
+    exe = str(tmp_path / "abi_from_c")
+    libdir = os.path.dirname(skv.LIB_PATH)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    src, "-o", exe, "-L", libdir, "-lsparse_kv", f"-Wl,-rpath,{libdir}"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "ok"
