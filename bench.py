@@ -83,9 +83,10 @@ def parse():
                     help="comma list of dense, sparse, art, window, art_imp, sparse2, dense_paged")
     ap.add_argument("--splits-per-shard", type=int, default=4, help="hybrid256k: inner splits per context shard")
     ap.add_argument("--sa-splits", type=int, default=32, help="hybrid256k: splits of a sink+window layer")
-    ap.add_argument("--workload", default="decode128k", choices=["decode128k", "art64k", "hybrid256k"],
+    ap.add_argument("--workload", default="decode128k", choices=["decode128k", "art64k", "hybrid256k", "dense32k"],
                     help="decode128k (default): the 128K batch-8 step above; art64k: ART on the 64K batch-32 "
-                         "recency workload vs dense; hybrid256k: 36-layer routed stack at 256K vs all-full")
+                         "recency workload vs dense; hybrid256k: 36-layer routed stack at 256K vs all-full; "
+                         "dense32k: dense split-KV decode + merge at 32K batch 8 (needle keys)")
     return ap.parse_args()
 
 
@@ -100,6 +101,8 @@ def main():
         return bench_art64k(args)
     if args.workload == "hybrid256k":
         return bench_hybrid256k(args)
+    if args.workload == "dense32k":
+        return bench_dense32k(args)
 
     import numpy as np
     import torch
@@ -411,6 +414,43 @@ def _line(args, metric, value, unit, ms, config, **extra):
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config}
     res.update(extra)
     print(json.dumps(res), flush=True)
+
+
+def bench_dense32k(args):
+    """Dense split-KV decode + merge at 32K context, batch 8 (Llama-3.1-8B layer shape, needle keys)."""
+    import numpy as np
+    import torch
+
+    import sparse_kv_amd as skv
+    import synth
+
+    W = synth.WORKLOADS[2]
+    B, Hq, Hkv, d, L = W["B"], W["Hq"], W["Hkv"], W["d"], W["L"]
+    dev = torch.device("cuda", 0)
+    inp = synth.make_inputs(2, B, Hq, Hkv, d, L, kind=W["kind"])
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    del inp
+    S = args.splits
+    m, l, o = skv.attn_decode_dense(q, k, v, None, num_splits=S)
+    out = skv.attn_merge_states(m, l, o)
+    tk, ts = _timer(), _timer()
+    for i in range(args.warmup + args.steps):
+        rec = i >= args.warmup
+        with (ts if rec else _timer()):
+            with (tk if rec else _timer()):
+                skv.attn_decode_dense(q, k, v, None, num_splits=S, m=m, l=l, o=o)
+            skv.attn_merge_states(m, l, o, out=out)
+    NB = L // 64
+    kv_bytes = B * Hkv * NB * 64 * d * 2 * 2
+    by = kv_bytes + B * Hq * d * 2 + B * Hq * d * 4
+    kb = kv_bytes + B * Hq * d * 2 + B * Hq * S * (d + 2) * 4
+    ms, kms = ts.avg_ms(), tk.avg_ms()
+    _line(args, "dense decode attention HBM GB/s, 32K ctx, batch 8", by / (ms * 1e-3) / 1e9, "GB/s", ms,
+          {"workload": "dense split-KV decode + merge, 32K context, batch 8, 32 q / 8 kv heads, d 128, bf16 KV, "
+                       "needle keys", "batch": B, "context": L, "splits": S, "parallelism": "single-gpu"},
+          tokens_per_s=round(B / (ms * 1e-3), 1), kernel_ms=round(kms, 5),
+          kernel_gbs=round(kb / (kms * 1e-3) / 1e9, 1), pct_of_peak_hbm=round(100 * by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2))
 
 
 def bench_art64k(args):
