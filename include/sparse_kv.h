@@ -48,7 +48,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = -1, /* a NULL required pointer, a bad size or dim      */
   ATTN_ERR_UNSUPPORTED = -2, /* valid but not built: d not in {64,128}, G > 8,
-                                a head's K slice above 2 GiB                  */
+                                a head's K slice above 2 GiB, and the per-
+                                function limits stated below                  */
   ATTN_ERR_HIP = -3,         /* a launch or HIP runtime call failed             */
   ATTN_ERR_WORKSPACE = -4    /* the workspace given is too small                */
 } attn_status;

@@ -35,10 +35,12 @@
 //     tokens, from the block table entry read through the scalar cache.
 // At the end the 4 waves' states are merged through LDS and the split's
 // (m, l, o) is written, o normalised, m in natural-log units.
-// Measured on MI355X at 128K context, batch 8: 6.93 TB/s with the pipelined
-// loop (the compiler then keeps one workgroup per CU) against 6.86 TB/s for
-// the plain loop at 2-3 workgroups per CU, which also re-fetches ~2% of K
-// from HBM because more half-read K lines are evicted from L2 in between.
+// Measured on MI355X at 128K context, batch 8: 6.99 TB/s (87% of the 8 TB/s
+// datasheet peak, 99% of a non-temporal streaming-read probe) with 4 splits
+// per (b, kv head), i.e. one workgroup per CU for the whole stream.  The
+// software-pipelined loop (one workgroup per CU by register use) beat a plain
+// loop at 2-3 workgroups per CU, 6.93 against 6.86 TB/s, and whole-line K
+// through LDS beat the operand-layout reads by another ~1%.
 #include "device_common.hpp"
 #include "kernels.hpp"
 

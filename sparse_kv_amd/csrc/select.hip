@@ -1,5 +1,7 @@
-// Content-aware block selection for gfx950: block centroids, group scores
-// against the query, and top-k with forced sink and recent blocks.
+// Content-aware block selection for gfx950: block centroids (built, or
+// refreshed after appends), group scores against the query, top-k with
+// forced sink and recent blocks, two-level (super-block) selection, and the
+// importance-first visit order.
 //
 // Method ("Squeezed Attention" blog, Q1 / Q2 steps 1-2): every group of keys
 // is represented by its centroid; the query is compared with the centroids
@@ -7,7 +9,9 @@
 // block and its centroid the block's mean key; the comparison is the scaled
 // dot product with the sum of the GQA group's queries, one score per KV head
 // and no softmax ("SparDA" summary, §2); the first block is always kept
-// ("ART" summary, §2.4, attention sink), as is a recent window.
+// ("ART" summary, §2.4, attention sink), as is a recent window.  Q2 step 4
+// (hierarchical clustering) adds a coarse level of super-blocks searched
+// first; ART §2.4 (importance first) orders blocks by the same scores.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
