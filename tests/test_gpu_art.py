@@ -59,6 +59,8 @@ def check_fetched(fetched, stop, inp):
     ("bf16-g4-d64", 2, 8, 2, 64, 64 * 40, None, "bf16"),
     ("f32-g1-d64", 1, 2, 2, 64, 64 * 30, None, "f32"),
     ("bf16-g8-d128", 1, 8, 1, 128, 64 * 36, None, "bf16"),
+    ("f32-g4-d128", 1, 8, 2, 128, 64 * 30, None, "f32"),
+    ("bf16-g6-d64", 2, 12, 2, 64, 64 * 32, [64 * 32, 64 * 27 + 5], "bf16"),
 ])
 def test_art_stop_positions_exact(label, B, Hq, Hkv, d, L, seq, dt):
     log(f"[art] {label}")

@@ -22,6 +22,8 @@ CASES = [
     ("bf16-g4-empty-row", 2, 8, 2, 128, 64 * 6, "bf16", "gauss", [0, 300], 3),
     ("f32-g4-d64", 2, 8, 2, 64, 64 * 11, "f32", "needles", [64 * 11, 64 * 5 + 7], 4),
     ("bf16-g3-d128", 1, 6, 2, 128, 64 * 12, "bf16", "gauss", [64 * 12 - 5], 3),
+    ("bf16-g6-d128-padded-heads", 2, 12, 2, 128, 64 * 13, "bf16", "needles", [64 * 13, 64 * 6 + 33], 4),
+    ("f32-g8-d128", 1, 8, 1, 128, 64 * 7, "f32", "gauss", [64 * 7 - 1], 2),
 ]
 
 
