@@ -8,7 +8,8 @@ blocks; keys a block-coherent Gaussian mixture, seeded synthetic data).
 One timed step runs every stage of the hot path over that batch:
   dense   split-KV decode + merge over all 2048 blocks      (full attention)
   sparse  centroid scores + top-k (10% + sink + last 64) + listed-block decode + merge
-  art     ART early-terminated decode, block 0 then most recent first
+  art     ART early-terminated decode, block 0 then most recent first (64 units,
+          each streamed by 4 workgroups through a device-memory ring)
   window  sink + recent-window decode + merge                 (routed SA layer)
 Optional (--stages ...,art_imp): centroid scores + importance order + ART
 visiting block 0 then blocks by descending centroid score.  Optional
@@ -66,6 +67,14 @@ def measured_dense_traffic(splits):
         return int(kv["dense_decode_traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def art_groups(units):
+    """Workgroups per (b, kv head) that attn_decode_art_ws launches on this device."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return min(4, cus // units) if units <= 128 and 2 * units <= cus else 1
 
 
 def parse():
@@ -182,6 +191,8 @@ def main():
     st_2 = (torch.empty((B, Hq, Ss), **f32), torch.empty((B, Hq, Ss), **f32), torch.empty((B, Hq, Ss, d), **f32))
     out_2 = torch.empty((B, Hq, d), **f32)
     order_i = torch.empty((B, Hkv, NB), dtype=torch.int32, device=dev)
+    # ART spreads each (b, kv head) over several CUs through this workspace when B * Hkv is small
+    art_ws = torch.empty(max(skv.attn_art_workspace_bytes(q, k0), 1), dtype=torch.uint8, device=dev)
     out_i = torch.empty((B, Hq, d), **f32)
     stop_i = torch.empty((B, Hq), dtype=torch.int32, device=dev)
     fetched_i = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
@@ -215,8 +226,8 @@ def main():
         if "art" in stages:
             ka, va = copies["art"]
             mark("art.0")
-            skv.attn_decode_art(q, ka, va, None, tau=tau, phi=phi, patience=patience, probe_dim=probe,
-                                out=out_a, stop_pos=stop, blocks_fetched=fetched)
+            skv.attn_decode_art_ws(q, ka, va, None, tau=tau, phi=phi, patience=patience, probe_dim=probe,
+                                   workspace=art_ws, out=out_a, stop_pos=stop, blocks_fetched=fetched)
             mark("art.1")
         if "window" in stages:
             kw, vw = copies["window"]
@@ -296,7 +307,7 @@ def main():
         paths["art"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), mean_stop=float(stp.mean()),
                             blocks_needed_per_unit=float(need.mean()),
                             blocks_fetched_per_unit=float(fetched.cpu().numpy().mean()),
-                            tokens_per_s=B / (ms * 1e-3))
+                            tokens_per_s=B / (ms * 1e-3), workgroups_per_unit=art_groups(B * Hkv))
     if "window" in stages:
         ms = avg_ms("window.0", "window.1")
         by = float(win_n.cpu().numpy().sum()) * kv_block + q_bytes + o_bytes

@@ -285,6 +285,31 @@ int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const v
                     int32_t* blocks_fetched, void* stream);
 
 /*
+ * attn_decode_art with a workspace, for batches too small to fill the chip.
+ * Defines: as attn_decode_art ("ART (Attention Run-time Termination)"
+ * summary, §2.1-2.4); same arguments, results and errors.  With
+ * B * Hkv <= 128 and at least 2 CUs per (b, kv head) on the current device,
+ * each (b, kv head) is streamed by up to 4 workgroups on different CUs that
+ * hand block states to one folding wave through the workspace; read-ahead
+ * past the stop is then up to 64 blocks per KV head.  Otherwise it runs as
+ * attn_decode_art and the workspace is not touched.
+ *   workspace        device memory of at least attn_art_workspace_bytes(dims)
+ *                    bytes (may be NULL when that is 0), used only by this
+ *                    call until it completes on `stream`; no initial contents.
+ * ATTN_ERR_INVALID_ARG for a NULL workspace that is needed,
+ * ATTN_ERR_WORKSPACE when workspace_bytes is too small.
+ */
+int attn_decode_art_ws(const attn_dims* dims, const void* q, const void* k, const void* v,
+                       const int32_t* seq_lens, const int32_t* order, float tau, float phi,
+                       int32_t patience, int32_t probe_dim, void* workspace, size_t workspace_bytes,
+                       float* out, int32_t* stop_pos, int32_t* blocks_fetched, void* stream);
+
+/* Workspace bytes attn_decode_art_ws needs for these dims: 0 when
+ * B * Hkv > 128 or on invalid dims, else 130.5 KiB (G <= 4) or 260.5 KiB
+ * (G > 4) per (b, kv head) at d = 128, about half that at d = 64. */
+size_t attn_art_workspace_bytes(const attn_dims* dims);
+
+/*
  * ART over a listed subset of blocks.
  * Defines: "ART (Attention Run-time Termination)" summary, §2.4 -- the stop
  * rule is a control layer that composes with KV selection: the visit order

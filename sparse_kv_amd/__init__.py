@@ -35,6 +35,8 @@ EXPORTS = (
     "attn_select_two_level",
     "attn_decode_sparse",
     "attn_decode_art",
+    "attn_decode_art_ws",
+    "attn_art_workspace_bytes",
     "attn_decode_art_list",
     "attn_order_blocks",
     "attn_decode_dense_paged",
@@ -87,6 +89,8 @@ _SIG = {
     "attn_select_two_level": [_D, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P],
     "attn_decode_sparse": [_D, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P],
     "attn_decode_art": [_D, _P, _P, _P, _P, _P, _F, _F, _I, _I, _P, _P, _P, _P],
+    "attn_decode_art_ws": [_D, _P, _P, _P, _P, _P, _F, _F, _I, _I, _P, ctypes.c_size_t, _P, _P, _P, _P],
+    "attn_art_workspace_bytes": [_D],
     "attn_decode_art_list": [_D, _P, _P, _P, _P, _P, _P, _I, _F, _F, _I, _I, _P, _P, _P, _P],
     "attn_order_blocks": [_D, _P, _P, _P, _P],
     "attn_decode_dense_paged": [_D, _P, _K, _P, _I, _I, _I, _P, _P, _P, _P],
@@ -110,7 +114,7 @@ def lib():
         for name, args in _SIG.items():
             fn = getattr(h, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_size_t if name == "attn_routed_workspace_bytes" else ctypes.c_int
+            fn.restype = ctypes.c_size_t if name.endswith("_workspace_bytes") else ctypes.c_int
         h.attn_status_string.argtypes = [ctypes.c_int]
         h.attn_status_string.restype = ctypes.c_char_p
         _lib = h
@@ -441,6 +445,41 @@ def attn_decode_art(q, k, v, seq_lens=None, order=None, tau=1e-3, phi=1e-4, pati
                                   float(tau), float(phi), int(patience), int(probe_dim), _ptr(out),
                                   _ptr(stop_pos), _ptr(blocks_fetched), _stream(dev))
     _check(st, "attn_decode_art")
+    return out, stop_pos, blocks_fetched
+
+
+def attn_art_workspace_bytes(q, k, scale=None):
+    """Bytes of workspace attn_decode_art_ws uses for these shapes (0: none)."""
+    dims = _dims_from(q, k, scale)
+    return int(lib().attn_art_workspace_bytes(ctypes.byref(dims)))
+
+
+def attn_decode_art_ws(q, k, v, seq_lens=None, order=None, tau=1e-3, phi=1e-4, patience=2, probe_dim=8,
+                       scale=None, workspace=None, out=None, stop_pos=None, blocks_fetched=None):
+    """attn_decode_art that may spread each (b, kv head) over several CUs through
+    `workspace` (uint8 device tensor of attn_art_workspace_bytes; allocated if None)."""
+    dev = q.device
+    dims = _dims_from(q, k, scale)
+    _need(q, "q", dev)
+    _need(k, "k", dev)
+    _need(v, "v", dev, k.dtype, k.shape)
+    seq = _seq(seq_lens, dims.batch, dev)
+    if order is not None:
+        _need(order, "order", dev, torch.int32, (dims.batch, dims.num_kv_heads, dims.max_blocks))
+    need = int(lib().attn_art_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    out = _out(out, (dims.batch, dims.num_q_heads, dims.head_dim), torch.float32, dev, "out")
+    stop_pos = _out(stop_pos, (dims.batch, dims.num_q_heads), torch.int32, dev, "stop_pos")
+    blocks_fetched = _out(blocks_fetched, (dims.batch, dims.num_kv_heads), torch.int32, dev, "blocks_fetched")
+    with _on_device(dev):
+        st = lib().attn_decode_art_ws(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(seq), _ptr(order),
+                                     float(tau), float(phi), int(patience), int(probe_dim), _ptr(workspace),
+                                     ws_bytes, _ptr(out), _ptr(stop_pos), _ptr(blocks_fetched), _stream(dev))
+    _check(st, "attn_decode_art_ws")
     return out, stop_pos, blocks_fetched
 
 

@@ -304,7 +304,8 @@ static int art_common(const attn_dims* dims, const void* q, const void* k, const
                       const int32_t* seq_lens, const int32_t* order, int32_t order_stride,
                       const int32_t* n_visit, float tau, float phi, int32_t patience,
                       int32_t probe_dim, float* out, int32_t* stop_pos, int32_t* blocks_fetched,
-                      void* stream, const attn_paged_kv* kv = nullptr) {
+                      void* stream, const attn_paged_kv* kv = nullptr, void* workspace = nullptr,
+                      size_t workspace_bytes = 0) {
   int st = check_dims(dims);
   if (st) return st;
   if (!q || !k || !v || !out || !stop_pos) return ATTN_ERR_INVALID_ARG;
@@ -339,7 +340,7 @@ static int art_common(const attn_dims* dims, const void* q, const void* k, const
     a.table_stride = kv->table_stride;
     a.pool_blocks = kv->pool_blocks;
   }
-  return hip_status(skv::launch_art(a, (hipStream_t)stream));
+  return hip_status(skv::launch_art(a, (hipStream_t)stream, workspace, workspace_bytes));
 }
 
 int attn_decode_art_paged(const attn_dims* dims, const void* q, const attn_paged_kv* kv, const int32_t* seq_lens,
@@ -359,6 +360,26 @@ int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const v
   const int32_t stride = dims ? dims->max_blocks : 0;
   return art_common(dims, q, k, v, seq_lens, order, stride, nullptr, tau, phi, patience, probe_dim,
                     out, stop_pos, blocks_fetched, stream);
+}
+
+size_t attn_art_workspace_bytes(const attn_dims* dims) {
+  if (check_dims(dims) != ATTN_OK) return 0;
+  const int64_t units = (int64_t)dims->batch * dims->num_kv_heads;
+  if (units > skv::kArtMcMaxUnits) return 0;
+  return skv::art_workspace_bytes((int32_t)units, dims->num_q_heads / dims->num_kv_heads, dims->head_dim);
+}
+
+int attn_decode_art_ws(const attn_dims* dims, const void* q, const void* k, const void* v,
+                       const int32_t* seq_lens, const int32_t* order, float tau, float phi,
+                       int32_t patience, int32_t probe_dim, void* workspace, size_t workspace_bytes,
+                       float* out, int32_t* stop_pos, int32_t* blocks_fetched, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  const size_t need = attn_art_workspace_bytes(dims);
+  if (need && !workspace) return ATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  return art_common(dims, q, k, v, seq_lens, order, dims->max_blocks, nullptr, tau, phi, patience, probe_dim,
+                    out, stop_pos, blocks_fetched, stream, nullptr, need ? workspace : nullptr, workspace_bytes);
 }
 
 int attn_decode_art_list(const attn_dims* dims, const void* q, const void* k, const void* v,

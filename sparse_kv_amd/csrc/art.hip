@@ -42,31 +42,190 @@ __device__ __forceinline__ void st_rel(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// NP producer waves, R ring slots (R also bounds the read-ahead).  Each
-// producer has a scratch area: its block's K rows (KROWS, padded by 16 bytes
-// per row so the MFMA-layout reads are free of bank conflicts), then the
-// block's softmax weights, which reuse the space once the logits are formed.
-template <typename T, int D, int GR, int NP, int R>
-struct ArtShared {
+// Per-wave LDS of a workgroup with NP producer waves: each producer's
+// scratch holds its block's K rows (KROWS, padded by 16 bytes per row so the
+// MFMA-layout reads are free of bank conflicts), then the block's softmax
+// weights, which reuse the space once the logits are formed; the folder's
+// output-fold weights.
+template <typename T, int D, int GR, int NP>
+struct ArtWaves {
   static constexpr int GP = 4 * GR;
-  static constexpr int kNP = NP, kR = R;
+  static constexpr int kNP = NP;
   static constexpr int kRowB = D * (int)sizeof(T);
   static constexpr bool kKRows = GR == 1 && kRowB <= 256;
   static constexpr int kKStride = kRowB + 16;
   static constexpr int kScratch = kKRows ? 64 * kKStride : 64 * GP * 4;
   __attribute__((aligned(16))) char scratch[NP][kScratch];
-  float slot_acc[R][GP][D];
-  float slot_m[R][GP];
-  float slot_l[R][GP];
-  int slot_pos[R];
   float fold_w[64];  // per (head, batch position) output weights
   float fold_a[GP];  // per head rescale of the running output
-  int folded;
-  int done;
-  int fetched;
 };
 
-// Producer wave pi: visit positions pi, pi + NP, ...  Each block is loaded
+// The ring through which producers hand block states (m, l, unnormalised
+// P.V of all channels, per query row) to the folder.  R slots: position t's
+// state lives in slot t % R and is marked by writing t into pos[t % R].  One
+// window word: the count of folded positions, or kDoneMark once the folder
+// has finished (producers then stop).
+constexpr int kDoneMark = 1 << 30;
+
+// In LDS: one workgroup per (b, kv head).  Acquire/release on LDS words.
+template <int GP, int D, int R>
+struct LdsRing {
+  static constexpr int kR = R;
+  __attribute__((aligned(16))) float acc[R][GP][D];
+  float m[R][GP];
+  float l[R][GP];
+  int pos[R];
+  int folded, fetched;
+  __device__ void init(int tid) {
+    if (tid < R) pos[tid] = -1;
+    if (tid == 0) {
+      folded = 0;
+      fetched = 0;
+    }
+  }
+  template <int E>
+  __device__ void put_acc(int s, int q, int col, const float (&v)[E]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[s][q][col + e] = v[e];
+  }
+  __device__ void put_ml(int s, int q, float mv, float lv) {
+    m[s][q] = mv;
+    l[s][q] = lv;
+  }
+  __device__ f32x4 acc4(int s, int q, int col) { return *(const f32x4*)&acc[s][q][col]; }
+  __device__ float m_at(int s, int q) { return m[s][q]; }
+  __device__ float l_at(int s, int q) { return l[s][q]; }
+  __device__ int window() { return ld_acq(&folded); }
+  __device__ void set_folded(int v) { st_rel(&folded, v); }
+  __device__ int poll(int s) { return ld_acq(&pos[s]); }
+  __device__ void acquire() {}
+
+  // one wave's LDS writes complete in order, so lane 0's release covers them
+  __device__ void publish(int s, int t, int lane) {
+    if (lane == 0) st_rel(&pos[s], t);
+  }
+  __device__ void count_fetch(int lane) {
+    if (lane == 0) atomicAdd(&fetched, 1);
+  }
+};
+
+// In global memory: the workgroups of one (b, kv head), on different CUs
+// and, in general, different XCDs.  Every access to the ring is a
+// device-scope one: stores write through to the device's coherence point
+// and loads read from it, so no wave ever writes back or invalidates a whole
+// L2 (with hundreds of producer waves doing so per block, that costs tens
+// of microseconds a block).  Order comes from completion: a producer waits
+// for its state stores to complete before it stores the position, the
+// folder issues its state loads only after it has read the position, and it
+// waits for them to complete before it advances the window.
+template <int GP, int D, int R>
+struct GlobalRing {
+  static constexpr int kR = R;
+  enum Ctrl { kFolded, kFetched, kExited, kNext, kFolder, kNumCtrl };
+  static constexpr uint32_t kPosOff = 0, kCtrlOff = 256;
+  static constexpr uint32_t kMOff = kCtrlOff + 256;
+  static constexpr uint32_t kLOff = kMOff + ((uint32_t)R * GP * 4 + 255) / 256 * 256;
+  static constexpr uint32_t kAccOff = kLOff + ((uint32_t)R * GP * 4 + 255) / 256 * 256;
+  static constexpr uint32_t kBytes = kAccOff + ((uint32_t)R * GP * D * 4 + 255) / 256 * 256;
+  static_assert(R * 4 <= 256, "slot positions fit their 256-byte area");
+  static constexpr int kSc1 = 16;  // cache policy: device scope
+  int* pos;
+  int* ctrl;
+  __amdgpu_buffer_rsrc_t rs;
+  int* local_fetched = nullptr;  // this workgroup's fetch count (LDS)
+  __device__ GlobalRing(char* ws, int unit) {
+    char* u = ws + (size_t)unit * kBytes;
+    pos = (int*)(u + kPosOff);
+    ctrl = (int*)(u + kCtrlOff);
+    rs = make_rsrc(u, kBytes);
+  }
+  static __device__ uint32_t acc_off(int s, int q, int col) {
+    return kAccOff + (((uint32_t)s * GP + q) * D + col) * 4;
+  }
+  template <int E>
+  __device__ void put_acc(int s, int q, int col, const float (&v)[E]) {
+    static_assert(E % 4 == 0, "16-byte stores");
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const u32x4 x = {__float_as_uint(v[e]), __float_as_uint(v[e + 1]), __float_as_uint(v[e + 2]),
+                       __float_as_uint(v[e + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(x, rs, (int)acc_off(s, q, col + e), 0, kSc1);
+    }
+  }
+  __device__ void put_ml(int s, int q, float mv, float lv) {
+    const int o = (s * GP + q) * 4;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mv), rs, (int)kMOff + o, 0, kSc1);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv), rs, (int)kLOff + o, 0, kSc1);
+  }
+  __device__ f32x4 acc4(int s, int q, int col) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)acc_off(s, q, col), 0, kSc1);
+    return f32x4{__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3])};
+  }
+  __device__ float m_at(int s, int q) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)kMOff + (s * GP + q) * 4, 0, kSc1));
+  }
+  __device__ float l_at(int s, int q) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)kLOff + (s * GP + q) * 4, 0, kSc1));
+  }
+  // vmcnt(0), with no memory access moved across it by the compiler
+  static __device__ void wait_memory() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+  }
+  __device__ int window() { return __hip_atomic_load(&ctrl[kFolded], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+  __device__ void set_folded(int v) {
+    wait_memory();  // the batch's slot loads are complete before the slots are handed back
+    __hip_atomic_store(&ctrl[kFolded], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ int poll(int s) { return __hip_atomic_load(&pos[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+  // state loads stay after the position loads that admitted them
+  __device__ void acquire() { asm volatile("" ::: "memory"); }
+  __device__ void publish(int s, int t, int lane) {
+    wait_memory();  // this wave's state stores are complete
+    if (lane == 0) __hip_atomic_store(&pos[s], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ void count_fetch(int lane) {
+    if (lane == 0) atomicAdd(local_fetched, 1);
+  }
+};
+
+// Single-workgroup form: the per-wave LDS plus the ring in LDS.
+template <typename T, int D, int GR, int NP, int R>
+struct ArtShared : ArtWaves<T, D, GR, NP> {
+  LdsRing<4 * GR, D, R> ring;
+};
+
+// Visit positions of one producer wave: a fixed stride (one workgroup per
+// unit), or claimed from a per-unit counter (several workgroups per unit,
+// whichever of them are resident).  Claims run one position ahead so their
+// round trip overlaps a block's work; a wave's claims increase, so the
+// smallest position not yet published always belongs to a wave that is at
+// it and whose window admits it.
+struct StridedPositions {
+  int t0, stride;
+  __device__ int first() { return t0; }
+  __device__ int next(int t) { return t + stride; }
+};
+struct ClaimedPositions {
+  int* counter;
+  int pending = 0;
+  __device__ void claim() {
+    if ((threadIdx.x & 63) == 0) pending = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ int take() {
+    const int t = __builtin_amdgcn_readfirstlane(pending);
+    claim();
+    return t;
+  }
+  __device__ int first() {
+    claim();
+    return take();
+  }
+  __device__ int next(int) { return take(); }
+};
+
+// Producer wave pi: visit positions from POS.  Each block is loaded
 // whole before its logits, softmax and P.V; with NP producers per
 // workgroup, NP blocks are in flight per CU.  V is read in the row layout
 // (whole 128-byte lines per instruction, non-temporal).  K is read the same
@@ -74,14 +233,14 @@ struct ArtShared {
 // the operand layout read straight from memory touches half of 16 lines
 // per instruction, which a CU streams about 30% slower than whole lines --
 // and with fewer units than CUs each unit runs at its CU's read limit.
-template <typename T, int D, int GR, typename SH>
-__device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, int g, int G, int L, int nb,
-                             int nv) {
+template <typename T, int D, int GR, typename SH, typename RING, typename POS>
+__device__ void art_producer(const ArtArgs& p, SH& sh, RING& ring, POS& pos, int pi, int unit, int b, int g, int G,
+                             int L, int nb, int nv) {
   using Gm = Geo<T, D>;
   constexpr int GP = 4 * GR;
   constexpr int E = Gm::E, CPR = Gm::CPR, TPI = Gm::TPI, KA = Gm::KA, ROWB = Gm::ROWB;
   constexpr bool BF = sizeof(T) == 2;
-  constexpr int kNP = SH::kNP, kR = SH::kR;
+  constexpr int kR = RING::kR;
   const int lane = threadIdx.x & 63;
   const int NBmax = p.NBmax;
 
@@ -114,12 +273,13 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
     return (p.order && t < nv) ? uniform_load(p.order, (int64_t)unit * p.order_stride + t) : 0;
   };
   auto block_from = [&](int t, int o) { return p.order ? clampi(o, 0, nb - 1) : (t == 0 ? 0 : nb - t); };
-  // read-ahead window: position t may start once t - kR has been folded
-  auto window_open = [&](int t) { return ld_acq(&sh.folded) > t - kR; };
+  // read-ahead window: position t may start once t - kR has been folded;
+  // false once the folder has finished
   auto window_wait = [&](int t) {
     while (true) {
-      if (ld_acq(&sh.done)) return false;
-      if (window_open(t)) return true;
+      const int f = ring.window();
+      if (f >= kDoneMark) return false;
+      if (f > t - kR) return true;
       __builtin_amdgcn_s_sleep(1);
     }
   };
@@ -157,7 +317,7 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
   // byte offset of block j in krs / vrs; a paged cache points them at the
   // block's own pool run (valid tokens only) and uses offset 0
   auto block_off = [&](int j) {
-    if (lane == 0) atomicAdd(&sh.fetched, 1);
+    ring.count_fetch(lane);
     if (paged) {
       const int ph = clampi(uniform_load(p.table, (int64_t)b * p.table_stride + j), 0, (int)(p.pool_blocks - 1));
       const size_t off = ((size_t)ph * p.Hkv + g) * (kBlock * ROWB);
@@ -169,7 +329,7 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
     return (uint32_t)j * kBlock * ROWB;
   };
 
-  int t = pi;
+  int t = pos.first();
   if (t >= nv || !window_wait(t)) return;
   int j = block_from(t, order_at(t));
   {
@@ -178,7 +338,7 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
     load_v(so);
   }
   while (true) {
-    const int tn = t + kNP;
+    const int tn = pos.next(t);
     const int onext = order_at(tn);
     k_to_operands();
     f32x4 sc[4];
@@ -262,18 +422,13 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, int pi, int unit, int b, 
     const int s = t % kR;
     if (lane < CPR) {
 #pragma unroll
-      for (int q = 0; q < GP; ++q)
-#pragma unroll
-        for (int e = 0; e < E; ++e) sh.slot_acc[s][q][lane * E + e] = ab[q][e];
+      for (int q = 0; q < GP; ++q) ring.put_acc(s, q, lane * E, ab[q]);
     }
     if (arow == 0) {
 #pragma unroll
-      for (int r = 0; r < GR; ++r) {
-        sh.slot_m[s][4 * r + kg] = mb[r];
-        sh.slot_l[s][4 * r + kg] = lb[r];
-      }
+      for (int r = 0; r < GR; ++r) ring.put_ml(s, 4 * r + kg, mb[r], lb[r]);
     }
-    if (lane == 0) st_rel(&sh.slot_pos[s], t);
+    ring.publish(s, t, lane);
 
     if (tn >= nv) return;
     if (!window_wait(tn)) return;
@@ -348,11 +503,11 @@ __device__ __forceinline__ void probe_of(float L, const float (&A)[PW], float& n
 // stop position.  The full output (all d channels) only needs the state at
 // the end of each batch (or at the stop): every lane folds its channel slice
 // with per-block weights exp2(m_j - M), staged in LDS.
-template <typename T, int D, int GR, typename SH>
-__device__ void art_folder(const ArtArgs& p, SH& sh, int b, int g, int G, int nv) {
+template <typename T, int D, int GR, typename SH, typename RING>
+__device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int b, int g, int G, int nv) {
   constexpr int GP = 4 * GR;
   constexpr int CH = 64 / GP;                // batch positions per head
-  constexpr int kR = SH::kR;
+  constexpr int kR = RING::kR;
   constexpr int NBT = CH < kR ? CH : kR;     // largest batch
   constexpr int FE = D / 16;                 // output channels per lane
   constexpr int PW = 16;                     // probe channels held (probe_dim <= 16)
@@ -378,23 +533,28 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, int b, int g, int G, int nv
   while (t0 < nv) {
     // length of the published run of positions t0, t0 + 1, ...
     const int tj = t0 + j;
-    const bool pub = j < NBT && tj < nv && ld_acq(&sh.slot_pos[tj % kR]) == tj;
+    const bool pub = j < NBT && tj < nv && ring.poll(tj % kR) == tj;
     const uint32_t pm = (uint32_t)__ballot(pub) & RM;  // group 0 checks every position
     const int n = __builtin_ctz(~pm);
     if (n == 0) {
       __builtin_amdgcn_s_sleep(1);
       continue;
     }
+    ring.acquire();
     const bool in = live && j < n;
     const int s = tj % kR;
     float m = -INFINITY, l = 0.f, a[PW];
 #pragma unroll
     for (int k = 0; k < PW; ++k) a[k] = 0.f;
     if (in) {
-      m = sh.slot_m[s][hh];
-      l = sh.slot_l[s][hh];
+      m = ring.m_at(s, hh);
+      l = ring.l_at(s, hh);
 #pragma unroll
-      for (int k = 0; k < PW; ++k) a[k] = k < P ? sh.slot_acc[s][hh][k] : 0.f;
+      for (int k4 = 0; k4 < PW / 4; ++k4) {
+        const f32x4 x = ring.acc4(s, hh, 4 * k4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[4 * k4 + e] = 4 * k4 + e < P ? x[e] : 0.f;
+      }
     }
     const float mb = m;
     scan_step<1, CH, PW>(j, m, l, a);
@@ -452,11 +612,15 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, int b, int g, int G, int nv
       for (int e = 0; e < FE; ++e) A[r][e] *= al;
 #pragma unroll
       for (int jj = 0; jj < NBT; ++jj) {
-        if (jj < n) {
-          const float w = sh.fold_w[hd * CH + jj];
-          const float* src_acc = &sh.slot_acc[(t0 + jj) % kR][hd][c * FE];
+        // positions past the batch reread its last slot with weight 0, so
+        // the loads need no branch
+        const float w = jj < n ? sh.fold_w[hd * CH + jj] : 0.f;
+        const int sj = (t0 + min(jj, n - 1)) % kR;
 #pragma unroll
-          for (int e = 0; e < FE; ++e) A[r][e] = fmaf(w, src_acc[e], A[r][e]);
+        for (int e4 = 0; e4 < FE; e4 += 4) {
+          const f32x4 x = ring.acc4(sj, hd, c * FE + e4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) A[r][e4 + e] = fmaf(w, x[e], A[r][e4 + e]);
         }
       }
     }
@@ -477,9 +641,9 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, int b, int g, int G, int nv
     // once every head has stopped, the window is not advanced past this
     // batch's start: read-ahead stays within R positions of the stop
     if (__ballot(live) == 0) break;
-    if (lane == 0) st_rel(&sh.folded, t0);
+    if (lane == 0) ring.set_folded(t0);
   }
-  if (lane == 0) st_rel(&sh.done, 1);
+  if (lane == 0) ring.set_folded(kDoneMark);
   // outputs: the frozen (or final) state of every head
 #pragma unroll
   for (int r = 0; r < GR; ++r) {
@@ -507,23 +671,95 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
   const int nb = (L + kBlock - 1) / kBlock;
   // visit positions: the whole sequence, or the first n_visit entries of the order
   const int nv = p.n_visit ? clampi(p.n_visit[unit], 0, min(nb, p.order_stride)) : nb;
-  if (threadIdx.x < R) sh.slot_pos[threadIdx.x] = -1;
-  if (threadIdx.x == 0) {
-    sh.folded = 0;
-    sh.done = 0;
-    sh.fetched = 0;
-  }
+  sh.ring.init(threadIdx.x);
   __syncthreads();
   if (w == 0) {
     // the folder is the serial chain of the kernel: let the SIMD arbiter
     // prefer it over the producer waves that share its SIMD
     __builtin_amdgcn_s_setprio(3);
-    art_folder<T, D, GR, SH>(p, sh, b, g, G, nv);
+    art_folder<T, D, GR>(p, sh, sh.ring, b, g, G, nv);
   }
   else
-    art_producer<T, D, GR, SH>(p, sh, __builtin_amdgcn_readfirstlane(w - 1), unit, b, g, G, L, nb, nv);
+  {
+    const int pi = __builtin_amdgcn_readfirstlane(w - 1);
+    StridedPositions pos{pi, NP};
+    art_producer<T, D, GR>(p, sh, sh.ring, pos, pi, unit, b, g, G, L, nb, nv);
+  }
   __syncthreads();
-  if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[unit] = sh.fetched;
+  if (threadIdx.x == 0 && p.blocks_fetched) p.blocks_fetched[unit] = sh.ring.fetched;
+}
+
+// Several workgroups per (b, kv head) unit, for grids that would leave most
+// CUs idle: one CU streams well under its share of HBM bandwidth, so a unit
+// on one CU is bound by that CU.  The unit's workgroups share a ring in
+// global memory; the first wave 0 to arrive folds, the other wave 0s leave,
+// and every producer wave claims positions from the unit's counter, so
+// progress never depends on which workgroups are resident.  The last
+// workgroup to finish reports the fetch count.
+template <int GP, int D, int R>
+__global__ __launch_bounds__(64) void art_ring_init(char* ws) {
+  GlobalRing<GP, D, R> ring(ws, blockIdx.x);
+  if (threadIdx.x < R) ring.pos[threadIdx.x] = -1;
+  if (threadIdx.x < GlobalRing<GP, D, R>::kNumCtrl) ring.ctrl[threadIdx.x] = 0;
+}
+
+template <typename T, int D, int GR, int NP>
+struct ArtMcShared : ArtWaves<T, D, GR, NP> {
+  int fetched;
+};
+
+template <typename T, int D, int GR, int NP, int R>
+__global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* ws, int groups) {
+  using SH = ArtMcShared<T, D, GR, NP>;
+  using RING = GlobalRing<4 * GR, D, R>;
+  __shared__ SH sh;
+  const int units = p.B * p.Hkv;
+  const int unit = blockIdx.x % units;
+  const int b = unit / p.Hkv, g = unit % p.Hkv;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int G = p.Hq / p.Hkv;
+  const int NBmax = p.NBmax;
+  const int L = clampi(p.seq_lens ? p.seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
+  const int nb = (L + kBlock - 1) / kBlock;
+  const int nv = p.n_visit ? clampi(p.n_visit[unit], 0, min(nb, p.order_stride)) : nb;
+  RING ring(ws, unit);
+  if (threadIdx.x == 0) sh.fetched = 0;
+  __syncthreads();
+  ring.local_fetched = &sh.fetched;
+  if (w == 0) {
+    int role = 0;
+    if (lane == 0) role = __hip_atomic_fetch_add(&ring.ctrl[RING::kFolder], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readfirstlane(role) == 0) {
+      __builtin_amdgcn_s_setprio(3);
+      art_folder<T, D, GR>(p, sh, ring, b, g, G, nv);
+    }
+  } else {
+    ClaimedPositions pos{&ring.ctrl[RING::kNext]};
+    art_producer<T, D, GR>(p, sh, ring, pos, __builtin_amdgcn_readfirstlane(w - 1), unit, b, g, G, L, nb, nv);
+  }
+  __syncthreads();
+  // the workgroup's fetch count is added (and complete) before it counts
+  // itself out; the last one out reads the unit's total
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&ring.ctrl[RING::kFetched], sh.fetched, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    RING::wait_memory();
+    const int before = __hip_atomic_fetch_add(&ring.ctrl[RING::kExited], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before == groups - 1 && p.blocks_fetched)
+      p.blocks_fetched[unit] = __hip_atomic_load(&ring.ctrl[RING::kFetched], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int D>
+constexpr size_t art_ring_bytes(int G) {
+  return G > 4 ? GlobalRing<8, D, kArtRingSlots>::kBytes : GlobalRing<4, D, kArtRingSlots>::kBytes;
+}
+
+template <typename T, int D, int GR>
+hipError_t launch_art_mc(const ArtArgs& a, char* ws, int groups, hipStream_t st) {
+  const int units = a.B * a.Hkv;
+  art_ring_init<4 * GR, D, kArtRingSlots><<<units, 64, 0, st>>>(ws);
+  art_mc_kernel<T, D, GR, 7, kArtRingSlots><<<units * groups, 8 * 64, 0, st>>>(a, ws, groups);
+  return hipGetLastError();
 }
 
 // With at least one (b, kv head) unit per CU the chip is bandwidth-bound and
@@ -532,13 +768,17 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
 // bandwidth, decides how far producers may run ahead: a 16-block window
 // lets them work on while it folds.
 template <typename T, int D>
-hipError_t launch_art_t(const ArtArgs& a, hipStream_t st) {
+hipError_t launch_art_t(const ArtArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int units = a.B * a.Hkv;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
+  if (ws && units <= kArtMcMaxUnits && 2 * units <= cus && ws_bytes >= (size_t)units * art_ring_bytes<D>(G)) {
+    const int groups = min(kArtMcMaxGroups, cus / units);
+    return G > 4 ? launch_art_mc<T, D, 2>(a, (char*)ws, groups, st) : launch_art_mc<T, D, 1>(a, (char*)ws, groups, st);
+  }
   const dim3 grid(units);
   const bool wide = units >= cus;
   if (G > 4) {
@@ -557,10 +797,16 @@ hipError_t launch_art_t(const ArtArgs& a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_art(const ArtArgs& a, hipStream_t st) {
+hipError_t launch_art(const ArtArgs& a, hipStream_t st, void* ws, size_t ws_bytes) {
   if (a.B == 0) return hipSuccess;
-  if (a.dtype == 1) return a.d == 128 ? launch_art_t<__bf16, 128>(a, st) : launch_art_t<__bf16, 64>(a, st);
-  return a.d == 128 ? launch_art_t<float, 128>(a, st) : launch_art_t<float, 64>(a, st);
+  if (a.dtype == 1)
+    return a.d == 128 ? launch_art_t<__bf16, 128>(a, ws, ws_bytes, st) : launch_art_t<__bf16, 64>(a, ws, ws_bytes, st);
+  return a.d == 128 ? launch_art_t<float, 128>(a, ws, ws_bytes, st) : launch_art_t<float, 64>(a, ws, ws_bytes, st);
+}
+
+size_t art_workspace_bytes(int32_t units, int32_t G, int32_t d) {
+  if (units < 1 || units > kArtMcMaxUnits) return 0;
+  return (size_t)units * (d == 128 ? art_ring_bytes<128>(G) : art_ring_bytes<64>(G));
 }
 
 }  // namespace skv

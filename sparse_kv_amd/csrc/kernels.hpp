@@ -68,7 +68,15 @@ hipError_t launch_score(const void* q, const float* c, const int32_t* seq_lens, 
 hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int32_t B, int32_t Hkv,
                        int32_t NBmax, int32_t k, int32_t n_sink, int32_t n_recent,
                        int32_t max_sel, int32_t* idx, int32_t* n_sel, hipStream_t st);
-hipError_t launch_art(const ArtArgs& a, hipStream_t st);
+// ART with several workgroups per (b, kv head) unit when the grid is small:
+// needs a workspace of art_workspace_bytes (0 beyond kArtMcMaxUnits units);
+// without one, or on a device with fewer than 2 CUs per unit, one workgroup
+// per unit.
+constexpr int kArtMcMaxUnits = 128;
+constexpr int kArtMcMaxGroups = 4;
+constexpr int kArtRingSlots = 64;
+hipError_t launch_art(const ArtArgs& a, hipStream_t st, void* ws = nullptr, size_t ws_bytes = 0);
+size_t art_workspace_bytes(int32_t units, int32_t G, int32_t d);
 // Two-level selection capacities: super-blocks per sequence, and fine
 // candidates (k_coarse * group) inside the opened super-blocks.
 constexpr int32_t kTwoLevelMaxSuper = 4096;

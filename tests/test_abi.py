@@ -167,6 +167,32 @@ def test_routed_workspace_and_validation(skv):
     assert big_sa == -1  # split counts are bounded
 
 
+def test_art_workspace_and_validation(skv):
+    lib = skv.lib()
+    d = dims()  # B = 2, Hkv = 2, G = 4, d = 128
+    per_unit_g4 = lib.attn_art_workspace_bytes(ctypes.byref(d)) // 4
+    assert per_unit_g4 > 0 and per_unit_g4 * 4 == lib.attn_art_workspace_bytes(ctypes.byref(d))
+    # the ring holds fp32 states: twice the query heads per slot, twice the bytes
+    per_unit_g8 = lib.attn_art_workspace_bytes(ctypes.byref(dims(num_q_heads=16))) // 4
+    assert 1.9 < per_unit_g8 / per_unit_g4 < 2.1
+    assert lib.attn_art_workspace_bytes(ctypes.byref(dims(head_dim=64))) < 4 * per_unit_g4
+    assert lib.attn_art_workspace_bytes(ctypes.byref(dims(batch=64))) == 128 * per_unit_g4
+    assert lib.attn_art_workspace_bytes(ctypes.byref(dims(batch=65))) == 0  # beyond 128 units: none used
+    assert lib.attn_art_workspace_bytes(ctypes.byref(dims(batch=0))) == 0
+    assert lib.attn_art_workspace_bytes(ctypes.byref(dims(head_dim=96))) == 0
+    assert lib.attn_art_workspace_bytes(None) == 0
+    need = lib.attn_art_workspace_bytes(ctypes.byref(d))
+    args = (FAKE, FAKE, FAKE, None, None, 1e-3, 1e-4, 2, 8)
+    call = lambda ws, nbytes, dd=d: lib.attn_decode_art_ws(ctypes.byref(dd), *args, ws, nbytes, FAKE, FAKE, None,
+                                                           None)
+    assert call(None, need) == -1       # a needed workspace is missing
+    assert call(FAKE, need - 1) == -4   # too small
+    assert lib.attn_decode_art_ws(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, 1e-3, 1e-4, 0, 8, FAKE, need,
+                                  FAKE, FAKE, None, None) == -1  # the attn_decode_art checks still apply
+    assert call(None, 0, dims(head_dim=96)) == -2
+    assert call(None, 0, dims(batch=0)) == 0  # nothing to do, nothing needed
+
+
 def test_status_strings(skv):
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(skv.attn_status_string(code), str) and skv.attn_status_string(code)

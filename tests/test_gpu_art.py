@@ -34,26 +34,37 @@ def art_inputs(cfg, B, Hq, Hkv, d, L, seq=None, dtype="bf16", recent=64 * 8, boo
     raise AssertionError("could not draw inputs with ART decision margins")
 
 
-def run_art(inp, order=None, tau=TAU, phi=PHI, p=P, probe=PROBE):
+# "one": attn_decode_art (one workgroup per (b, kv head)); "ws": attn_decode_art_ws,
+# which at these batch sizes spreads each (b, kv head) over several workgroups
+PATHS = ["one", "ws"]
+READ_AHEAD = {"one": 16, "ws": 64}
+
+
+def run_art(inp, order=None, tau=TAU, phi=PHI, p=P, probe=PROBE, path="one", workspace=None):
     import sparse_kv_amd as skv
 
     q, k, v, sl = upload(inp)
     o = None if order is None else torch.from_numpy(np.ascontiguousarray(order, dtype=np.int32)).cuda()
-    out, stop, fetched = skv.attn_decode_art(q, k, v, sl, order=o, tau=tau, phi=phi, patience=p, probe_dim=probe)
+    kw = dict(order=o, tau=tau, phi=phi, patience=p, probe_dim=probe)
+    if path == "ws":
+        out, stop, fetched = skv.attn_decode_art_ws(q, k, v, sl, workspace=workspace, **kw)
+    else:
+        out, stop, fetched = skv.attn_decode_art(q, k, v, sl, **kw)
     torch.cuda.synchronize()
     return out.cpu().numpy(), stop.cpu().numpy(), fetched.cpu().numpy()
 
 
-def check_fetched(fetched, stop, inp):
+def check_fetched(fetched, stop, inp, path="one"):
     B, Hq, Hkv, _, _ = inp.shape
     G = Hq // Hkv
     for b in range(B):
         nb = -(-int(inp.seq_lens[b]) // 64)
         for g in range(Hkv):
             need = int(stop[b, g * G:(g + 1) * G].max()) + 1
-            assert need <= fetched[b, g] <= min(nb, need + 16), (b, g, need, fetched[b, g])
+            assert need <= fetched[b, g] <= min(nb, need + READ_AHEAD[path]), (b, g, need, fetched[b, g])
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("label,B,Hq,Hkv,d,L,seq,dt", [
     ("bf16-g4-d128", 2, 8, 2, 128, 64 * 48, [64 * 48, 64 * 40 + 17], "bf16"),
     ("bf16-g4-d64", 2, 8, 2, 64, 64 * 40, None, "bf16"),
@@ -62,38 +73,40 @@ def check_fetched(fetched, stop, inp):
     ("f32-g4-d128", 1, 8, 2, 128, 64 * 30, None, "f32"),
     ("bf16-g6-d64", 2, 12, 2, 64, 64 * 32, [64 * 32, 64 * 27 + 5], "bf16"),
 ])
-def test_art_stop_positions_exact(label, B, Hq, Hkv, d, L, seq, dt):
-    log(f"[art] {label}")
+def test_art_stop_positions_exact(label, B, Hq, Hkv, d, L, seq, dt, path):
+    log(f"[art] {label} ({path})")
     inp, ref_out, ref_stop = art_inputs(40, B, Hq, Hkv, d, L, seq=seq, dtype=dt)
-    out, stop, fetched = run_art(inp)
+    out, stop, fetched = run_art(inp, path=path)
     log(f"  stops {ref_stop.ravel().tolist()}")
     assert np.array_equal(stop, ref_stop), (stop, ref_stop)
     assert_close(out, ref_out, TOL, "ART output")
-    check_fetched(fetched, stop, inp)
+    check_fetched(fetched, stop, inp, path)
     assert (ref_stop < np.array([-(-int(s) // 64) for s in inp.seq_lens])[:, None] - 1).any(), \
         "the case should stop early somewhere"
 
 
-def test_art_special_cases_reduce_to_dense():
-    log("[art] tau = phi = 0, probe off, patience > nb, tau = phi = inf")
+@pytest.mark.parametrize("path", PATHS)
+def test_art_special_cases_reduce_to_dense(path):
+    log(f"[art] tau = phi = 0, probe off, patience > nb, tau = phi = inf ({path})")
     inp = synth.make_inputs(41, 2, 8, 2, 128, 64 * 20, kind="recency", seq_lens=[64 * 20, 64 * 11 + 5],
                             recent_tokens=64 * 4)
     qf, kf, vf = inp.f64()
     dense = oracle.decode_dense(qf, kf, vf, inp.seq_lens, inp.scale)
     nbs = np.array([20, 12])[:, None]
     for tau, phi, p, probe in ((0.0, 0.0, 1, 8), (1.0, 1.0, 2, 0), (math.inf, math.inf, 30, 8)):
-        out, stop, fetched = run_art(inp, tau=tau, phi=phi, p=p, probe=probe)
+        out, stop, fetched = run_art(inp, tau=tau, phi=phi, p=p, probe=probe, path=path)
         assert (stop == nbs - 1).all(), (tau, phi, p, probe, stop)
         assert (fetched == nbs).all()
         assert_close(out, dense, TOL, f"dense-equivalent ART tau={tau} probe={probe}")
-    out, stop, fetched = run_art(inp, tau=math.inf, phi=math.inf, p=1, probe=8)
+    out, stop, fetched = run_art(inp, tau=math.inf, phi=math.inf, p=1, probe=8, path=path)
     assert (stop == 1).all()
     ref_out, ref_stop, _ = oracle.art_decode(qf, kf, vf, inp.seq_lens, inp.scale, math.inf, math.inf, 1, 8)
     assert_close(out, ref_out, TOL, "stop after two blocks")
 
 
-def test_art_custom_visit_order():
-    log("[art] custom visit orders starting with block 0")
+@pytest.mark.parametrize("path", PATHS)
+def test_art_custom_visit_order(path):
+    log(f"[art] custom visit orders starting with block 0 ({path})")
     B, Hq, Hkv, L = 1, 8, 2, 64 * 24
     nb = 24
     r = np.random.default_rng(3)
@@ -102,22 +115,43 @@ def test_art_custom_visit_order():
         order[0, g] = [0] + list(r.permutation(np.arange(1, nb)))
     inp = synth.make_inputs(42, B, Hq, Hkv, 128, L, kind="recency", recent_tokens=64 * 6)
     qf, kf, vf = inp.f64()
-    out, stop, _ = run_art(inp, order=order, tau=0.0, phi=0.0)
+    out, stop, _ = run_art(inp, order=order, tau=0.0, phi=0.0, path=path)
     assert (stop == nb - 1).all()
     assert_close(out, oracle.decode_dense(qf, kf, vf, inp.seq_lens, inp.scale), TOL, "order-invariant dense")
     inp, ref_out, ref_stop = art_inputs(43, B, Hq, Hkv, 128, L, recent=64 * 6, order=order)
-    out, stop, _ = run_art(inp, order=order)
+    out, stop, _ = run_art(inp, order=order, path=path)
     assert np.array_equal(stop, ref_stop)
     assert_close(out, ref_out, TOL, "custom-order ART output")
 
 
-def test_art_empty_and_single_block_rows():
-    log("[art] rows with 0 and 1 blocks")
+@pytest.mark.parametrize("path", PATHS)
+def test_art_empty_and_single_block_rows(path):
+    log(f"[art] rows with 0 and 1 blocks ({path})")
     inp = synth.make_inputs(44, 3, 4, 1, 128, 64 * 4, kind="gauss", seq_lens=[0, 30, 64 * 4])
-    out, stop, fetched = run_art(inp)
+    out, stop, fetched = run_art(inp, path=path)
     qf, kf, vf = inp.f64()
     ref_out, ref_stop, _ = oracle.art_decode(qf, kf, vf, inp.seq_lens, inp.scale, TAU, PHI, P, PROBE)
     assert stop[0].tolist() == [-1] * 4 and not out[0].any() and fetched[0, 0] == 0
     assert stop[1].tolist() == [0] * 4 and fetched[1, 0] == 1
     assert np.array_equal(stop, ref_stop)
     assert_close(out, ref_out, TOL, "output")
+
+
+def test_art_workspace_reused_across_calls():
+    """One workspace, three calls in a row (G = 4, then G = 8 with a smaller
+    batch, then G = 4 again): every call starts from a clean ring."""
+    import sparse_kv_amd as skv
+
+    log("[art] workspace reuse")
+    cases = [(45, 2, 8, 2, [64 * 30, 64 * 22 + 9]), (46, 1, 8, 1, [64 * 26]), (47, 2, 8, 2, [64 * 25, 64 * 30])]
+    need = max(skv.attn_art_workspace_bytes(torch.empty(B, Hq, 128, dtype=torch.bfloat16),
+                                            torch.empty(B, Hkv, 64 * 30, 128, dtype=torch.bfloat16))
+               for _, B, Hq, Hkv, _ in cases)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws.fill_(0x7f)  # contents from an earlier user must not matter
+    for seed, B, Hq, Hkv, seq in cases:
+        inp, ref_out, ref_stop = art_inputs(seed, B, Hq, Hkv, 128, 64 * 30, seq=seq)
+        out, stop, fetched = run_art(inp, path="ws", workspace=ws)
+        assert np.array_equal(stop, ref_stop), (seed, stop, ref_stop)
+        assert_close(out, ref_out, TOL, f"ART output, seed {seed}")
+        check_fetched(fetched, stop, inp, "ws")

@@ -122,6 +122,57 @@ def test_art_64k_batch32_stop_positions():
         assert need <= fetched[b, g] <= need + 8, (b, g, need, fetched[b, g])
 
 
+def test_art_128k_batch8_across_workgroups():
+    """ART in the benchmark's 128K batch-8 configuration (block 0, then newest
+    first), through attn_decode_art_ws: 64 (b, kv head) units, each streamed
+    by several workgroups.  Units whose every decision clears the margins are
+    checked exactly against the oracle; all units against the one-workgroup
+    kernel (same stops wherever both clear the margins, outputs to TOL)."""
+    W3, W4 = synth.WORKLOADS[3], synth.WORKLOADS[4]
+    B, Hq, Hkv, d, L = W3["B"], W3["Hq"], W3["Hkv"], W3["d"], W3["L"]
+    tau, phi, p, probe = W4["tau"], W4["phi"], W4["patience"], W4["probe_dim"]
+    t = time.time()
+    inp = synth.make_inputs(3, B, Hq, Hkv, d, L, kind="mixture")
+    log(f"[full] ART 128K batch 8 across workgroups: inputs in {time.time() - t:.1f}s")
+    import sparse_kv_amd as skv
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    kw = dict(tau=tau, phi=phi, patience=p, probe_dim=probe)
+    ws = torch.empty(skv.attn_art_workspace_bytes(q, k), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+    out, stop, fetched = skv.attn_decode_art_ws(q, k, v, None, workspace=ws, **kw)
+    out1, stop1, fetched1 = skv.attn_decode_art(q, k, v, None, **kw)
+    torch.cuda.synchronize()
+    out, stop, fetched = out.cpu().numpy(), stop.cpu().numpy(), fetched.cpu().numpy()
+    out1, stop1 = out1.cpu().numpy(), stop1.cpu().numpy()
+    G = Hq // Hkv
+    log(f"  mean stop {stop.mean():.1f}, max {stop.max()}, mean fetched {fetched.mean():.1f} "
+        f"(one workgroup: {fetched1.float().mean().item():.1f}); {int((stop == stop1).sum())} of {stop.size} "
+        f"stops equal the one-workgroup kernel's")
+    units = SAMPLE + [(b, g) for b in range(B) for g in range(Hkv) if (b, g) not in SAMPLE]
+    checked = 0
+    for b, g in units:
+        qf, kf, vf, seq = unit_f64(inp, b, g)
+        ro, rs, tr = oracle.art_decode(qf, kf, vf, seq, inp.scale, tau, phi, p, probe)
+        if not all(art_margin_ok(x, tau, phi) for x in tr.values()):
+            continue
+        assert stop[b, g * G:(g + 1) * G].tolist() == rs[0].tolist(), f"stop positions of unit ({b},{g})"
+        assert stop1[b, g * G:(g + 1) * G].tolist() == rs[0].tolist(), f"one-workgroup stops of unit ({b},{g})"
+        assert_close(out[b, g * G:(g + 1) * G], ro[0], TOL, f"ART unit ({b},{g})")
+        need = int(rs.max()) + 1
+        assert need <= fetched[b, g] <= need + 64, (b, g, need, fetched[b, g])
+        checked += 1
+        if checked == 3:
+            break
+    assert checked >= 2, "too few units clear the ART decision margins"
+    same = stop == stop1
+    for b in range(B):
+        for g in range(Hkv):
+            if same[b, g * G:(g + 1) * G].all():
+                assert_close(out[b, g * G:(g + 1) * G], out1[b, g * G:(g + 1) * G], TOL, f"unit ({b},{g}) vs one")
+    assert same.mean() > 0.9
+
+
 def test_routed_36_layer_stack_256k():
     W = synth.WORKLOADS[5]
     B, Hq, Hkv, d, L = W["B"], W["Hq"], W["Hkv"], W["d"], W["L"]
