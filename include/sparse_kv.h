@@ -290,9 +290,10 @@ int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const v
  * summary, §2.1-2.4); same arguments, results and errors.  With
  * B * Hkv <= 128 and at least 2 CUs per (b, kv head) on the current device,
  * each (b, kv head) is streamed by up to 4 workgroups on different CUs that
- * hand block states to one folding wave through the workspace; read-ahead
- * past the stop is then up to 64 blocks per KV head.  Otherwise it runs as
- * attn_decode_art and the workspace is not touched.
+ * hand block states to per-head folding waves through the workspace;
+ * read-ahead past the stop is then at most max(32, T + 1) blocks, and at
+ * most 128, per KV head.  Otherwise it runs as attn_decode_art and the
+ * workspace is not touched.
  *   workspace        device memory of at least attn_art_workspace_bytes(dims)
  *                    bytes (may be NULL when that is 0), used only by this
  *                    call until it completes on `stream`; no initial contents.
@@ -305,7 +306,7 @@ int attn_decode_art_ws(const attn_dims* dims, const void* q, const void* k, cons
                        float* out, int32_t* stop_pos, int32_t* blocks_fetched, void* stream);
 
 /* Workspace bytes attn_decode_art_ws needs for these dims: 0 when
- * B * Hkv > 128 or on invalid dims, else 130.5 KiB (G <= 4) or 260.5 KiB
+ * B * Hkv > 128 or on invalid dims, else 261 KiB (G <= 4) or 521 KiB
  * (G > 4) per (b, kv head) at d = 128, about half that at d = 64. */
 size_t attn_art_workspace_bytes(const attn_dims* dims);
 

@@ -45,8 +45,9 @@ __device__ __forceinline__ void st_rel(int* p, int v) {
 // Per-wave LDS of a workgroup with NP producer waves: each producer's
 // scratch holds its block's K rows (KROWS, padded by 16 bytes per row so the
 // MFMA-layout reads are free of bank conflicts), then the block's softmax
-// weights, which reuse the space once the logits are formed; the folder's
+// weights, which reuse the space once the logits are formed; the folders'
 // output-fold weights.
+constexpr int kMaxFolders = 8;
 template <typename T, int D, int GR, int NP>
 struct ArtWaves {
   static constexpr int GP = 4 * GR;
@@ -56,8 +57,8 @@ struct ArtWaves {
   static constexpr int kKStride = kRowB + 16;
   static constexpr int kScratch = kKRows ? 64 * kKStride : 64 * GP * 4;
   __attribute__((aligned(16))) char scratch[NP][kScratch];
-  float fold_w[64];  // per (head, batch position) output weights
-  float fold_a[GP];  // per head rescale of the running output
+  float fold_w[kMaxFolders][64];  // per folder: (head, batch position) output weights
+  float fold_a[kMaxFolders][GP];  // per folder: per head rescale of the running output
 };
 
 // The ring through which producers hand block states (m, l, unnormalised
@@ -66,6 +67,12 @@ struct ArtWaves {
 // window word: the count of folded positions, or kDoneMark once the folder
 // has finished (producers then stop).
 constexpr int kDoneMark = 1 << 30;
+// Read-ahead allowed once f positions are folded: the ring size, but no more
+// than max(32, f), so a head that stops early wastes few blocks.
+template <int R>
+__device__ __forceinline__ int window_span(int f) {
+  return min(R, max(32, f));
+}
 
 // In LDS: one workgroup per (b, kv head).  Acquire/release on LDS words.
 template <int GP, int D, int R>
@@ -95,8 +102,14 @@ struct LdsRing {
   __device__ f32x4 acc4(int s, int q, int col) { return *(const f32x4*)&acc[s][q][col]; }
   __device__ float m_at(int s, int q) { return m[s][q]; }
   __device__ float l_at(int s, int q) { return l[s][q]; }
+  static constexpr int kMaxBatch = R;
   __device__ int window() { return ld_acq(&folded); }
-  __device__ void set_folded(int v) { st_rel(&folded, v); }
+  __device__ void set_folded(int, int v) { st_rel(&folded, v); }
+  template <int FE>
+  __device__ void acc_row(int s, int q, int col, float (&x)[FE]) {
+#pragma unroll
+    for (int e = 0; e < FE; ++e) x[e] = acc[s][q][col + e];
+  }
   __device__ int poll(int s) { return ld_acq(&pos[s]); }
   __device__ void acquire() {}
 
@@ -118,16 +131,21 @@ struct LdsRing {
 // for its state stores to complete before it stores the position, the
 // folder issues its state loads only after it has read the position, and it
 // waits for them to complete before it advances the window.
-template <int GP, int D, int R>
+template <int GP, int D, int R, int NF>
 struct GlobalRing {
   static constexpr int kR = R;
-  enum Ctrl { kFolded, kFetched, kExited, kNext, kFolder, kNumCtrl };
-  static constexpr uint32_t kPosOff = 0, kCtrlOff = 256;
-  static constexpr uint32_t kMOff = kCtrlOff + 256;
+  static constexpr int kMaxBatch = R / 2;  // the producers work on the other half
+  // control words, on separate 128-byte lines: the folders' counts of
+  // folded positions (polled by every producer), the position claims, the
+  // accounting words
+  enum Ctrl { kFolded = 0, kNext = 32, kFetched = 64, kExited, kFolder, kNumCtrl = 96 };
+  static_assert(NF <= 8 && R * 4 <= 512, "control and position areas");
+  static constexpr uint32_t kPosOff = 0, kCtrlOff = 512;
+  static constexpr uint32_t kMOff = kCtrlOff + 512;
+  static_assert(kNumCtrl * 4 <= 512, "control area");
   static constexpr uint32_t kLOff = kMOff + ((uint32_t)R * GP * 4 + 255) / 256 * 256;
   static constexpr uint32_t kAccOff = kLOff + ((uint32_t)R * GP * 4 + 255) / 256 * 256;
   static constexpr uint32_t kBytes = kAccOff + ((uint32_t)R * GP * D * 4 + 255) / 256 * 256;
-  static_assert(R * 4 <= 256, "slot positions fit their 256-byte area");
   static constexpr int kSc1 = 16;  // cache policy: device scope
   int* pos;
   int* ctrl;
@@ -173,10 +191,37 @@ struct GlobalRing {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     asm volatile("" ::: "memory");
   }
-  __device__ int window() { return __hip_atomic_load(&ctrl[kFolded], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-  __device__ void set_folded(int v) {
+  // the least count of folded positions over the folders (kDoneMark: all done)
+  __device__ int window() {
+    const int lane = threadIdx.x & 63;
+    int v = lane < NF ? __hip_atomic_load(&ctrl[kFolded + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : kDoneMark;
+    v = min(v, __shfl_xor(v, 1));
+    v = min(v, __shfl_xor(v, 2));
+    v = min(v, __shfl_xor(v, 4));
+    return __builtin_amdgcn_readfirstlane(v);
+  }
+  __device__ void set_folded(int f, int v) {
     wait_memory();  // the batch's slot loads are complete before the slots are handed back
-    __hip_atomic_store(&ctrl[kFolded], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ctrl[kFolded + f], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  template <int FE>
+  __device__ void acc_row(int s, int q, int col, float (&x)[FE]) {
+    if constexpr (FE % 4 == 0) {
+#pragma unroll
+      for (int e = 0; e < FE; e += 4) {
+        const f32x4 v = acc4(s, q, col + e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[e + i] = v[i];
+      }
+    } else if constexpr (FE == 2) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)acc_off(s, q, col), 0, kSc1);
+      x[0] = __uint_as_float(v[0]);
+      x[1] = __uint_as_float(v[1]);
+    } else {
+      static_assert(FE == 1, "row slice of 1, 2 or 4k floats");
+      x[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)acc_off(s, q, col), 0, kSc1));
+    }
   }
   __device__ int poll(int s) { return __hip_atomic_load(&pos[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
   // state loads stay after the position loads that admitted them
@@ -273,13 +318,15 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, RING& ring, POS& pos, int
     return (p.order && t < nv) ? uniform_load(p.order, (int64_t)unit * p.order_stride + t) : 0;
   };
   auto block_from = [&](int t, int o) { return p.order ? clampi(o, 0, nb - 1) : (t == 0 ? 0 : nb - t); };
-  // read-ahead window: position t may start once t - kR has been folded;
-  // false once the folder has finished
+  // read-ahead window: position t may start once the folders are within
+  // window_span of it; false once they have finished.  It is read afresh
+  // for every block: a look per block keeps read-ahead (and over-fetch past
+  // the stop) in check and shows at once that the folders have finished.
   auto window_wait = [&](int t) {
     while (true) {
       const int f = ring.window();
       if (f >= kDoneMark) return false;
-      if (f > t - kR) return true;
+      if (f > t - window_span<kR>(f)) return true;
       __builtin_amdgcn_s_sleep(1);
     }
   };
@@ -430,8 +477,7 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, RING& ring, POS& pos, int
     }
     ring.publish(s, t, lane);
 
-    if (tn >= nv) return;
-    if (!window_wait(tn)) return;
+    if (tn >= nv || !window_wait(tn)) return;
     j = block_from(tn, onext);
     const uint32_t so = block_off(j);
     load_k(so);
@@ -454,11 +500,15 @@ __device__ __forceinline__ void merge_into(float me, float le, const float (&ae)
   m = M;
 }
 
-// row_shr:K within rows of 16 lanes (the caller discards lanes whose source
-// lies outside their group).
-template <int K>
+// The value of lane - K for groups of CH lanes (the caller discards lanes
+// whose source lies outside their group): row_shr:K when groups stay within
+// rows of 16 lanes, a lane permute when they span rows.
+template <int K, int CH>
 __device__ __forceinline__ float shr(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + K, 0xF, 0xF, false));
+  if constexpr (CH <= 16)
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + K, 0xF, 0xF, false));
+  else
+    return __shfl(x, ((int)threadIdx.x - K) & 63);
 }
 
 // One inclusive-scan step over groups of CH lanes: lanes at group position
@@ -466,10 +516,10 @@ __device__ __forceinline__ float shr(float x) {
 template <int K, int CH, int PW>
 __device__ __forceinline__ void scan_step(int j, float& m, float& l, float (&a)[PW]) {
   if constexpr (K < CH) {
-    const float me = shr<K>(m), le = shr<K>(l);
+    const float me = shr<K, CH>(m), le = shr<K, CH>(l);
     float ae[PW];
 #pragma unroll
-    for (int k = 0; k < PW; ++k) ae[k] = shr<K>(a[k]);
+    for (int k = 0; k < PW; ++k) ae[k] = shr<K, CH>(a[k]);
     if (j >= K) merge_into<PW>(me, le, ae, m, l, a);
   }
 }
@@ -491,51 +541,54 @@ __device__ __forceinline__ void probe_of(float L, const float (&A)[PW], float& n
   for (int k = 0; k < PW; ++k) u[k] *= i1;
 }
 
-// The folder wave.  It folds published block states strictly in visit order,
+// A folder wave.  It folds published block states strictly in visit order,
 // as a one-block-at-a-time streaming kernel would, but a batch at a time:
-// every consecutive position already published (up to CH = 64 / (4 GR)) is
-// taken at once.  In the scan layout lane (h, j) = h * CH + j holds head h's
-// state of the batch's block j; an inclusive scan over j (DPP row shifts)
-// gives the running state after every block of the batch, from which each
-// lane evaluates the stop rule for its position.  Consecutive-stable runs
-// come from the ballot of the per-position decisions, so one batch costs
-// about as much as one block did.  A head that stops keeps its state at its
-// stop position.  The full output (all d channels) only needs the state at
-// the end of each batch (or at the stop): every lane folds its channel slice
-// with per-block weights exp2(m_j - M), staged in LDS.
-template <typename T, int D, int GR, typename SH, typename RING>
-__device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int b, int g, int G, int nv) {
-  constexpr int GP = 4 * GR;
-  constexpr int CH = 64 / GP;                // batch positions per head
+// every consecutive position already published (up to CH = 64 / HPW, and
+// the ring's batch cap) is taken at once.  Folder f owns heads
+// f * HPW .. f * HPW + HPW - 1.  In the scan layout lane (h, j) = h * CH + j
+// holds head h's state of the batch's block j; an inclusive scan over j
+// (DPP row shifts, lane permutes past 16) gives the running state after
+// every block of the batch, from which each lane evaluates the stop rule
+// for its position.  Consecutive-stable runs come from the ballot of the
+// per-position decisions, so one batch costs about as much as one block
+// did.  A head that stops keeps its state at its stop position.  The full
+// output (all d channels) only needs the state at the end of each batch (or
+// at the stop): lane (h, j) folds channels j * D / CH .. of head h with
+// per-block weights exp2(m_j - M), staged in LDS.  PW probe channels are
+// carried (probe_dim <= PW).
+template <typename T, int D, int HPW, int PW, typename SH, typename RING>
+__device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int f, int b, int g, int G, int nv) {
+  constexpr int CH = 64 / HPW;  // batch positions per head; lanes per head
   constexpr int kR = RING::kR;
-  constexpr int NBT = CH < kR ? CH : kR;     // largest batch
-  constexpr int FE = D / 16;                 // output channels per lane
-  constexpr int PW = 16;                     // probe channels held (probe_dim <= 16)
-  constexpr uint32_t RM = (CH == 32) ? 0xffffffffu : ((1u << CH) - 1u);
+  constexpr int NBT = CH < RING::kMaxBatch ? CH : RING::kMaxBatch;  // largest batch
+  constexpr int FE = D / CH;    // output channels per lane
+  constexpr uint64_t RM = CH == 64 ? ~0ull : ((1ull << CH) - 1ull);
+  static_assert(PW % 4 == 0 && PW <= 16 && FE >= 1, "layout");
   const int lane = threadIdx.x & 63;
-  const int hh = lane / CH, j = lane % CH;   // scan layout
-  const int q4 = lane >> 4, c = lane & 15;   // output layout
+  const int hh = lane / CH, j = lane % CH;  // scan and output layout
+  const int head = f * HPW + hh;            // head of the unit
   const int P = p.probe_dim;
+  float* fold_w = sh.fold_w[f];
+  float* fold_a = sh.fold_a[f];
 
   // running state of head hh, identical in the CH lanes of its group
   float cM = -INFINITY, cL = 0.f, cA[PW];
 #pragma unroll
   for (int k = 0; k < PW; ++k) cA[k] = 0.f;
   int ccnt = 0, dstop = -1;
-  bool live = hh < G;
-  float A[GR][FE];
+  bool live = head < G;
+  float A[FE];
 #pragma unroll
-  for (int r = 0; r < GR; ++r)
-#pragma unroll
-    for (int e = 0; e < FE; ++e) A[r][e] = 0.f;
+  for (int e = 0; e < FE; ++e) A[e] = 0.f;
 
   int t0 = 0;
-  while (t0 < nv) {
+  // a folder with no real head (padded groups) takes no part
+  while (__ballot(live) != 0 && t0 < nv) {
     // length of the published run of positions t0, t0 + 1, ...
     const int tj = t0 + j;
     const bool pub = j < NBT && tj < nv && ring.poll(tj % kR) == tj;
-    const uint32_t pm = (uint32_t)__ballot(pub) & RM;  // group 0 checks every position
-    const int n = __builtin_ctz(~pm);
+    const uint64_t pm = (uint64_t)__ballot(pub) & RM;  // group 0 checks every position
+    const int n = ~pm == 0 ? 64 : __builtin_ctzll(~pm);
     if (n == 0) {
       __builtin_amdgcn_s_sleep(1);
       continue;
@@ -547,11 +600,11 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int b, int g, i
 #pragma unroll
     for (int k = 0; k < PW; ++k) a[k] = 0.f;
     if (in) {
-      m = ring.m_at(s, hh);
-      l = ring.l_at(s, hh);
+      m = ring.m_at(s, head);
+      l = ring.l_at(s, head);
 #pragma unroll
       for (int k4 = 0; k4 < PW / 4; ++k4) {
-        const f32x4 x = ring.acc4(s, hh, 4 * k4);
+        const f32x4 x = ring.acc4(s, head, 4 * k4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) a[4 * k4 + e] = 4 * k4 + e < P ? x[e] : 0.f;
       }
@@ -561,15 +614,17 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int b, int g, i
     scan_step<2, CH, PW>(j, m, l, a);
     scan_step<4, CH, PW>(j, m, l, a);
     scan_step<8, CH, PW>(j, m, l, a);
+    scan_step<16, CH, PW>(j, m, l, a);
+    scan_step<32, CH, PW>(j, m, l, a);
     // state after block j = carry (+) scan_j
     merge_into<PW>(cM, cL, cA, m, l, a);
     float nrm, u[PW];
     probe_of<PW>(l, a, nrm, u);
     float cn, cu[PW];
     probe_of<PW>(cL, cA, cn, cu);
-    float np = shr<1>(nrm), up[PW];
+    float np = shr<1, CH>(nrm), up[PW];
 #pragma unroll
-    for (int k = 0; k < PW; ++k) up[k] = shr<1>(u[k]);
+    for (int k = 0; k < PW; ++k) up[k] = shr<1, CH>(u[k]);
     if (j == 0) {
       np = cn;
 #pragma unroll
@@ -586,12 +641,12 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int b, int g, i
     const float dd = (nrm > 0.f && np > 0.f) ? 0.5f * u2 : INFINITY;
     const bool st = in && tj >= 1 && ds < p.tau && dd < p.phi;
     // consecutive stable steps ending at j (plus the run carried in)
-    const uint32_t rowb = (uint32_t)(__ballot(st) >> (hh * CH)) & RM;
-    const uint32_t z = ~rowb & ((2u << j) - 1u);
-    const int run = z == 0 ? j + 1 + ccnt : j - (31 - __builtin_clz(z));
+    const uint64_t rowb = ((uint64_t)__ballot(st) >> (hh * CH)) & RM;
+    const uint64_t z = ~rowb & ((2ull << j) - 1ull);
+    const int run = z == 0 ? j + 1 + ccnt : j - (63 - __builtin_clzll(z));
     const bool hit = st && run >= p.patience;
-    const uint32_t rowh = (uint32_t)(__ballot(hit) >> (hh * CH)) & RM;
-    const int jend = rowh ? __builtin_ctz(rowh) : n - 1;
+    const uint64_t rowh = ((uint64_t)__ballot(hit) >> (hh * CH)) & RM;
+    const int jend = rowh ? __builtin_ctzll(rowh) : n - 1;
     const int src = hh * CH + jend;
     // the new running state: the state at jend
     const float nM = __shfl(m, src), nL = __shfl(l, src);
@@ -601,26 +656,25 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int b, int g, i
     for (int k = 0; k < PW; ++k) nA[k] = k < P ? __shfl(a[k], src) : 0.f;
     // weights of the batch's blocks in the new state, staged for the output fold
     const float nMs = nM == -INFINITY ? 0.f : nM;
-    sh.fold_w[lane] = (in && j <= jend) ? fast_exp2(mb - nMs) : 0.f;
-    if (j == 0 && hh < GP) sh.fold_a[hh] = live ? fast_exp2(cM - nMs) : 1.f;
+    fold_w[lane] = (in && j <= jend) ? fast_exp2(mb - nMs) : 0.f;
+    if (j == 0) fold_a[hh] = live ? fast_exp2(cM - nMs) : 1.f;
     wave_lds_exchange();  // the weights are read by the other lanes
+    {
+      const float al = fold_a[hh];
 #pragma unroll
-    for (int r = 0; r < GR; ++r) {
-      const int hd = 4 * r + q4;
-      const float al = sh.fold_a[hd];
+      for (int e = 0; e < FE; ++e) A[e] *= al;
+      // chunks of positions whose rows are all loaded before any is used;
+      // positions past the batch reread its last slot with weight 0
+      constexpr int CK = (64 / FE < 32 ? 64 / FE : 32) < NBT ? (64 / FE < 32 ? 64 / FE : 32) : NBT;
+      for (int j0 = 0; j0 < n; j0 += CK) {
+        float x[CK][FE];
 #pragma unroll
-      for (int e = 0; e < FE; ++e) A[r][e] *= al;
+        for (int jj = 0; jj < CK; ++jj) ring.acc_row((t0 + min(j0 + jj, n - 1)) % kR, head, j * FE, x[jj]);
 #pragma unroll
-      for (int jj = 0; jj < NBT; ++jj) {
-        // positions past the batch reread its last slot with weight 0, so
-        // the loads need no branch
-        const float w = jj < n ? sh.fold_w[hd * CH + jj] : 0.f;
-        const int sj = (t0 + min(jj, n - 1)) % kR;
+        for (int jj = 0; jj < CK; ++jj) {
+          const float w = j0 + jj < n ? fold_w[hh * CH + j0 + jj] : 0.f;
 #pragma unroll
-        for (int e4 = 0; e4 < FE; e4 += 4) {
-          const f32x4 x = ring.acc4(sj, hd, c * FE + e4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) A[r][e4 + e] = fmaf(w, x[e], A[r][e4 + e]);
+          for (int e = 0; e < FE; ++e) A[e] = fmaf(w, x[jj][e], A[e]);
         }
       }
     }
@@ -639,23 +693,27 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int b, int g, i
     }
     t0 += n;
     // once every head has stopped, the window is not advanced past this
-    // batch's start: read-ahead stays within R positions of the stop
+    // batch's start: read-ahead stays within the window of the stop
     if (__ballot(live) == 0) break;
-    if (lane == 0) ring.set_folded(t0);
+    if (lane == 0) ring.set_folded(f, t0);
   }
-  if (lane == 0) ring.set_folded(kDoneMark);
+  if (lane == 0) ring.set_folded(f, kDoneMark);
   // outputs: the frozen (or final) state of every head
+  if (head < G) {
+    float* dst = p.out + ((size_t)b * p.Hq + (size_t)g * G + head) * D + j * FE;
 #pragma unroll
-  for (int r = 0; r < GR; ++r) {
-    const int hd = 4 * r + q4;
-    const float Lr = __shfl(cL, hd * CH);
-    if (hd < G) {
-      float* dst = p.out + ((size_t)b * p.Hq + (size_t)g * G + hd) * D + c * FE;
-#pragma unroll
-      for (int e = 0; e < FE; ++e) dst[e] = Lr > 0.f ? A[r][e] / Lr : 0.f;
-    }
+    for (int e = 0; e < FE; ++e) dst[e] = cL > 0.f ? A[e] / cL : 0.f;
+    if (j == 0) p.stop_pos[(size_t)b * p.Hq + (size_t)g * G + head] = dstop >= 0 ? dstop : nv - 1;
   }
-  if (j == 0 && hh < G) p.stop_pos[(size_t)b * p.Hq + (size_t)g * G + hh] = dstop >= 0 ? dstop : nv - 1;
+}
+
+// probe_dim <= 8 carries half the probe channels through the scan
+template <typename T, int D, int HPW, typename SH, typename RING>
+__device__ void art_fold(const ArtArgs& p, SH& sh, RING& ring, int f, int b, int g, int G, int nv) {
+  if (p.probe_dim <= 8)
+    art_folder<T, D, HPW, 8>(p, sh, ring, f, b, g, G, nv);
+  else
+    art_folder<T, D, HPW, 16>(p, sh, ring, f, b, g, G, nv);
 }
 
 template <typename T, int D, int GR, int NP, int R>
@@ -677,7 +735,7 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
     // the folder is the serial chain of the kernel: let the SIMD arbiter
     // prefer it over the producer waves that share its SIMD
     __builtin_amdgcn_s_setprio(3);
-    art_folder<T, D, GR>(p, sh, sh.ring, b, g, G, nv);
+    art_fold<T, D, 4 * GR>(p, sh, sh.ring, 0, b, g, G, nv);
   }
   else
   {
@@ -697,43 +755,47 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
 // progress never depends on which workgroups are resident.  The last
 // workgroup to finish reports the fetch count.
 template <int GP, int D, int R>
-__global__ __launch_bounds__(64) void art_ring_init(char* ws) {
-  GlobalRing<GP, D, R> ring(ws, blockIdx.x);
+__global__ __launch_bounds__(128) void art_ring_init(char* ws) {
+  using RING = GlobalRing<GP, D, R, GP>;
+  RING ring(ws, blockIdx.x);
   if (threadIdx.x < R) ring.pos[threadIdx.x] = -1;
-  if (threadIdx.x < GlobalRing<GP, D, R>::kNumCtrl) ring.ctrl[threadIdx.x] = 0;
+  if (threadIdx.x < RING::kNumCtrl) ring.ctrl[threadIdx.x] = 0;
 }
 
 template <typename T, int D, int GR, int NP>
 struct ArtMcShared : ArtWaves<T, D, GR, NP> {
   int fetched;
+  int role;  // 0: this workgroup's first waves fold
 };
 
 template <typename T, int D, int GR, int NP, int R>
 __global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* ws, int groups) {
   using SH = ArtMcShared<T, D, GR, NP>;
-  using RING = GlobalRing<4 * GR, D, R>;
+  constexpr int NF = 4 * GR;  // one folder wave per query head
+  static_assert(NF <= kMaxFolders && NF <= NP + 1, "folder waves");
+  using RING = GlobalRing<4 * GR, D, R, NF>;
   __shared__ SH sh;
   const int units = p.B * p.Hkv;
   const int unit = blockIdx.x % units;
   const int b = unit / p.Hkv, g = unit % p.Hkv;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
   const int G = p.Hq / p.Hkv;
   const int NBmax = p.NBmax;
   const int L = clampi(p.seq_lens ? p.seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
   const int nb = (L + kBlock - 1) / kBlock;
   const int nv = p.n_visit ? clampi(p.n_visit[unit], 0, min(nb, p.order_stride)) : nb;
   RING ring(ws, unit);
-  if (threadIdx.x == 0) sh.fetched = 0;
+  if (threadIdx.x == 0) {
+    sh.fetched = 0;
+    sh.role = __hip_atomic_fetch_add(&ring.ctrl[RING::kFolder], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
   ring.local_fetched = &sh.fetched;
-  if (w == 0) {
-    int role = 0;
-    if (lane == 0) role = __hip_atomic_fetch_add(&ring.ctrl[RING::kFolder], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__builtin_amdgcn_readfirstlane(role) == 0) {
-      __builtin_amdgcn_s_setprio(3);
-      art_folder<T, D, GR>(p, sh, ring, b, g, G, nv);
-    }
-  } else {
+  const bool folds = sh.role == 0;
+  if (folds && w < NF) {
+    __builtin_amdgcn_s_setprio(3);
+    art_fold<T, D, 1>(p, sh, ring, __builtin_amdgcn_readfirstlane(w), b, g, G, nv);
+  } else if (w > 0) {
     ClaimedPositions pos{&ring.ctrl[RING::kNext]};
     art_producer<T, D, GR>(p, sh, ring, pos, __builtin_amdgcn_readfirstlane(w - 1), unit, b, g, G, L, nb, nv);
   }
@@ -751,13 +813,13 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* 
 
 template <int D>
 constexpr size_t art_ring_bytes(int G) {
-  return G > 4 ? GlobalRing<8, D, kArtRingSlots>::kBytes : GlobalRing<4, D, kArtRingSlots>::kBytes;
+  return G > 4 ? GlobalRing<8, D, kArtRingSlots, 8>::kBytes : GlobalRing<4, D, kArtRingSlots, 4>::kBytes;
 }
 
 template <typename T, int D, int GR>
 hipError_t launch_art_mc(const ArtArgs& a, char* ws, int groups, hipStream_t st) {
   const int units = a.B * a.Hkv;
-  art_ring_init<4 * GR, D, kArtRingSlots><<<units, 64, 0, st>>>(ws);
+  art_ring_init<4 * GR, D, kArtRingSlots><<<units, 128, 0, st>>>(ws);
   art_mc_kernel<T, D, GR, 7, kArtRingSlots><<<units * groups, 8 * 64, 0, st>>>(a, ws, groups);
   return hipGetLastError();
 }

@@ -74,7 +74,7 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int32_t B, 
 // per unit.
 constexpr int kArtMcMaxUnits = 128;
 constexpr int kArtMcMaxGroups = 4;
-constexpr int kArtRingSlots = 64;
+constexpr int kArtRingSlots = 128;
 hipError_t launch_art(const ArtArgs& a, hipStream_t st, void* ws = nullptr, size_t ws_bytes = 0);
 size_t art_workspace_bytes(int32_t units, int32_t G, int32_t d);
 // Two-level selection capacities: super-blocks per sequence, and fine

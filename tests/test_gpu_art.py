@@ -37,7 +37,7 @@ def art_inputs(cfg, B, Hq, Hkv, d, L, seq=None, dtype="bf16", recent=64 * 8, boo
 # "one": attn_decode_art (one workgroup per (b, kv head)); "ws": attn_decode_art_ws,
 # which at these batch sizes spreads each (b, kv head) over several workgroups
 PATHS = ["one", "ws"]
-READ_AHEAD = {"one": 16, "ws": 64}
+READ_AHEAD = {"one": 16, "ws": 128}
 
 
 def run_art(inp, order=None, tau=TAU, phi=PHI, p=P, probe=PROBE, path="one", workspace=None):
