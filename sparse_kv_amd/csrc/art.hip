@@ -62,10 +62,11 @@ struct ArtWaves {
 };
 
 // The ring through which producers hand block states (m, l, unnormalised
-// P.V of all channels, per query row) to the folder.  R slots: position t's
+// P.V of all channels, per query row) to the folders.  R slots: position t's
 // state lives in slot t % R and is marked by writing t into pos[t % R].  One
-// window word: the count of folded positions, or kDoneMark once the folder
-// has finished (producers then stop).
+// window word per folder: its count of folded positions, or kDoneMark once
+// it has finished.  Producers go by the least of them and stop when every
+// folder has finished.
 constexpr int kDoneMark = 1 << 30;
 // Read-ahead allowed once f positions are folded: the ring size, but no more
 // than max(32, f), so a head that stops early wastes few blocks.
