@@ -65,17 +65,21 @@ def test_topk_exact_on_given_scores(k, ns, nr):
             assert (idx[b, g, len(want):] == -1).all()
 
 
-def test_topk_large_rows_radix_paths():
-    log("[select] top-k on 4096-block rows")
+@pytest.mark.parametrize("NB", [2048, 4096])
+def test_topk_large_rows_radix_paths(NB):
+    # 2048-block rows take the one-wave register select, longer rows the workgroup radix select
+    log(f"[select] top-k on {NB}-block rows")
     r = np.random.default_rng(9)
-    B, Hkv, NB = 2, 2, 4096
+    B, Hkv = 2, 2
     s = (r.standard_normal((B, Hkv, NB)) * 3).astype(np.float32)
     s[0, 1] = np.round(s[0, 1] * 4) / 4  # heavy ties
-    s[1, 0, 100:200] = s[1, 0, 3000]  # ties at the boundary region
-    seq = np.array([64 * NB, 64 * 3000 - 17], dtype=np.int32)
+    s[1, 0, 100:200] = s[1, 0, NB * 3 // 4]  # ties at the boundary region
+    s[1, 1, 7] = -0.0
+    s[1, 1, 8] = 0.0
+    seq = np.array([64 * NB, 64 * (NB * 3 // 4) - 17], dtype=np.int32)
     import sparse_kv_amd as skv
 
-    for k, ns, nr in ((410, 1, 64), (1, 1, 0), (3000, 2, 7)):
+    for k, ns, nr in ((NB // 10, 1, 64), (1, 1, 0), (NB * 3 // 4, 2, 7), (NB, 0, 0), (NB // 2, 0, 0)):
         idx, n = skv.attn_select_topk(upload_scores(s), torch.from_numpy(seq).cuda(), k=k, n_sink_blocks=ns,
                                       n_recent_blocks=nr)
         torch.cuda.synchronize()
