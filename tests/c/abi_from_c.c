@@ -51,6 +51,14 @@ int main(void) {
   CHECK(attn_decode_dense_paged(&d, fake, &kv, NULL, 0, -1, 4, ff, ff, ff, NULL) == ATTN_ERR_INVALID_ARG);
   CHECK(attn_routed_workspace_bytes(&d, 8, 4, 32) > 0);
   CHECK(attn_routed_workspace_bytes(&d, 0, 4, 32) == 0);
+  {
+    const size_t art_ws = attn_art_workspace_bytes(&d);
+    CHECK(art_ws > 0);
+    CHECK(attn_decode_art_ws(&d, fake, fake, fake, NULL, NULL, 1e-3f, 1e-4f, 2, 8, NULL, art_ws, ff, fi, NULL,
+                             NULL) == ATTN_ERR_INVALID_ARG);
+    CHECK(attn_decode_art_ws(&d, fake, fake, fake, NULL, NULL, 1e-3f, 1e-4f, 2, 8, fake, art_ws - 1, ff, fi, NULL,
+                             NULL) == ATTN_ERR_WORKSPACE);
+  }
   d.batch = 0;
   CHECK(attn_decode_dense(&d, fake, fake, fake, NULL, 0, -1, 4, ff, ff, ff, NULL) == ATTN_OK);
   if (fails == 0) printf("ok\n");
