@@ -264,12 +264,18 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
+    # the timed steps carry no events (a stage-boundary event costs a few
+    # microseconds); a second pass of the same steps records the per-stage
+    # and dense-kernel events for the breakdown and the roofline
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step(False)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
 
     def avg_ms(a, b):
         xs = [e0.elapsed_time(e1) for e0, e1 in zip(ev[a], ev[b])]
