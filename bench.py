@@ -257,8 +257,9 @@ def main():
             mark("art_imp.score")
             skv.attn_order_blocks(scores_i, None, out=order_i)
             mark("art_imp.order")
-            skv.attn_decode_art(q, ki, vi, None, order=order_i, tau=tau, phi=phi, patience=patience,
-                                probe_dim=probe, out=out_i, stop_pos=stop_i, blocks_fetched=fetched_i)
+            skv.attn_decode_art_ws(q, ki, vi, None, order=order_i, tau=tau, phi=phi, patience=patience,
+                                   probe_dim=probe, workspace=art_ws, out=out_i, stop_pos=stop_i,
+                                   blocks_fetched=fetched_i)
             mark("art_imp.1")
 
     for _ in range(args.warmup):

@@ -260,13 +260,16 @@ def test_importance_first_art_128k_batch8():
     inj = order_h.copy()
     for (b, g), oo in oracle_rows.items():
         inj[b, g] = oo
-    out2, stop2, _ = skv.attn_decode_art(q, k, v, None, order=torch.from_numpy(inj).cuda(), tau=tau, phi=phi,
-                                         patience=p, probe_dim=probe)
-    torch.cuda.synchronize()
-    out2, stop2 = out2.cpu().numpy(), stop2.cpu().numpy()
-    for (b, g), (ro, rs) in ref.items():
-        assert stop2[b, g * G:(g + 1) * G].tolist() == rs.tolist(), f"stop positions of unit ({b},{g})"
-        assert_close(out2[b, g * G:(g + 1) * G], ro, TOL, f"importance-first ART unit ({b},{g})")
+    inj_d = torch.from_numpy(inj).cuda()
+    kw = dict(order=inj_d, tau=tau, phi=phi, patience=p, probe_dim=probe)
+    # one workgroup per unit, and the benchmark's path: several workgroups per unit
+    for name, fn in (("one", skv.attn_decode_art), ("ws", skv.attn_decode_art_ws)):
+        out2, stop2, _ = fn(q, k, v, None, **kw)
+        torch.cuda.synchronize()
+        out2, stop2 = out2.cpu().numpy(), stop2.cpu().numpy()
+        for (b, g), (ro, rs) in ref.items():
+            assert stop2[b, g * G:(g + 1) * G].tolist() == rs.tolist(), f"{name}: stop positions of unit ({b},{g})"
+            assert_close(out2[b, g * G:(g + 1) * G], ro, TOL, f"{name}: importance-first ART unit ({b},{g})")
 
 
 def test_two_level_selection_128k_batch8():
