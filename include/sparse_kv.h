@@ -305,6 +305,22 @@ int attn_decode_art_ws(const attn_dims* dims, const void* q, const void* k, cons
                        int32_t patience, int32_t probe_dim, void* workspace, size_t workspace_bytes,
                        float* out, int32_t* stop_pos, int32_t* blocks_fetched, void* stream);
 
+/*
+ * attn_decode_art_list and attn_decode_art_paged across workgroups.
+ * Defines: as attn_decode_art_list and attn_decode_art_paged ("ART (Attention
+ * Run-time Termination)" summary, §2.1-2.4); same arguments, results and
+ * errors, plus the workspace, its size and its use as in attn_decode_art_ws.
+ */
+int attn_decode_art_list_ws(const attn_dims* dims, const void* q, const void* k, const void* v,
+                            const int32_t* seq_lens, const int32_t* block_list, const int32_t* n_list,
+                            int32_t max_list, float tau, float phi, int32_t patience, int32_t probe_dim,
+                            void* workspace, size_t workspace_bytes, float* out, int32_t* stop_pos,
+                            int32_t* blocks_fetched, void* stream);
+int attn_decode_art_paged_ws(const attn_dims* dims, const void* q, const attn_paged_kv* kv,
+                             const int32_t* seq_lens, const int32_t* order, float tau, float phi,
+                             int32_t patience, int32_t probe_dim, void* workspace, size_t workspace_bytes,
+                             float* out, int32_t* stop_pos, int32_t* blocks_fetched, void* stream);
+
 /* Workspace bytes attn_decode_art_ws needs for these dims: 0 when
  * B * Hkv > 128 or on invalid dims, else 261 KiB (G <= 4) or 521 KiB
  * (G > 4) per (b, kv head) at d = 128, about half that at d = 64. */

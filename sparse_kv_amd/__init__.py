@@ -36,6 +36,8 @@ EXPORTS = (
     "attn_decode_sparse",
     "attn_decode_art",
     "attn_decode_art_ws",
+    "attn_decode_art_list_ws",
+    "attn_decode_art_paged_ws",
     "attn_art_workspace_bytes",
     "attn_decode_art_list",
     "attn_order_blocks",
@@ -91,6 +93,8 @@ _SIG = {
     "attn_decode_art": [_D, _P, _P, _P, _P, _P, _F, _F, _I, _I, _P, _P, _P, _P],
     "attn_decode_art_ws": [_D, _P, _P, _P, _P, _P, _F, _F, _I, _I, _P, ctypes.c_size_t, _P, _P, _P, _P],
     "attn_art_workspace_bytes": [_D],
+    "attn_decode_art_list_ws": [_D, _P, _P, _P, _P, _P, _P, _I, _F, _F, _I, _I, _P, ctypes.c_size_t, _P, _P, _P, _P],
+    "attn_decode_art_paged_ws": [_D, _P, _K, _P, _P, _F, _F, _I, _I, _P, ctypes.c_size_t, _P, _P, _P, _P],
     "attn_decode_art_list": [_D, _P, _P, _P, _P, _P, _P, _I, _F, _F, _I, _I, _P, _P, _P, _P],
     "attn_order_blocks": [_D, _P, _P, _P, _P],
     "attn_decode_dense_paged": [_D, _P, _K, _P, _I, _I, _I, _P, _P, _P, _P],
@@ -448,6 +452,16 @@ def attn_decode_art(q, k, v, seq_lens=None, order=None, tau=1e-3, phi=1e-4, pati
     return out, stop_pos, blocks_fetched
 
 
+def _art_workspace(dims, workspace, dev):
+    """(workspace, bytes) for the ART calls across workgroups; allocated when None and needed."""
+    need = int(lib().attn_art_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", dev)
+    return workspace, (workspace.numel() * workspace.element_size() if workspace is not None else 0)
+
+
 def attn_art_workspace_bytes(q, k, scale=None):
     """Bytes of workspace attn_decode_art_ws uses for these shapes (0: none)."""
     dims = _dims_from(q, k, scale)
@@ -466,12 +480,7 @@ def attn_decode_art_ws(q, k, v, seq_lens=None, order=None, tau=1e-3, phi=1e-4, p
     seq = _seq(seq_lens, dims.batch, dev)
     if order is not None:
         _need(order, "order", dev, torch.int32, (dims.batch, dims.num_kv_heads, dims.max_blocks))
-    need = int(lib().attn_art_workspace_bytes(ctypes.byref(dims)))
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    if workspace is not None:
-        _need(workspace, "workspace", dev)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    workspace, ws_bytes = _art_workspace(dims, workspace, dev)
     out = _out(out, (dims.batch, dims.num_q_heads, dims.head_dim), torch.float32, dev, "out")
     stop_pos = _out(stop_pos, (dims.batch, dims.num_q_heads), torch.int32, dev, "stop_pos")
     blocks_fetched = _out(blocks_fetched, (dims.batch, dims.num_kv_heads), torch.int32, dev, "blocks_fetched")
@@ -505,6 +514,32 @@ def attn_decode_art_list(q, k, v, block_list, n_list, seq_lens=None, tau=1e-3, p
                                        float(tau), float(phi), int(patience), int(probe_dim), _ptr(out),
                                        _ptr(stop_pos), _ptr(blocks_fetched), _stream(dev))
     _check(st, "attn_decode_art_list")
+    return out, stop_pos, blocks_fetched
+
+
+def attn_decode_art_list_ws(q, k, v, block_list, n_list, seq_lens=None, tau=1e-3, phi=1e-4, patience=2,
+                            probe_dim=8, scale=None, workspace=None, out=None, stop_pos=None, blocks_fetched=None):
+    """attn_decode_art_list that may spread each (b, kv head) over several CUs through `workspace`."""
+    dev = q.device
+    dims = _dims_from(q, k, scale)
+    _need(q, "q", dev)
+    _need(k, "k", dev)
+    _need(v, "v", dev, k.dtype, k.shape)
+    _need(block_list, "block_list", dev, torch.int32)
+    if block_list.dim() != 3 or tuple(block_list.shape[:2]) != (dims.batch, dims.num_kv_heads):
+        raise ValueError("block_list must be [B, Hkv, max_list]")
+    _need(n_list, "n_list", dev, torch.int32, (dims.batch, dims.num_kv_heads))
+    seq = _seq(seq_lens, dims.batch, dev)
+    workspace, ws_bytes = _art_workspace(dims, workspace, dev)
+    out = _out(out, (dims.batch, dims.num_q_heads, dims.head_dim), torch.float32, dev, "out")
+    stop_pos = _out(stop_pos, (dims.batch, dims.num_q_heads), torch.int32, dev, "stop_pos")
+    blocks_fetched = _out(blocks_fetched, (dims.batch, dims.num_kv_heads), torch.int32, dev, "blocks_fetched")
+    with _on_device(dev):
+        st = lib().attn_decode_art_list_ws(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(seq),
+                                          _ptr(block_list), _ptr(n_list), int(block_list.shape[2]),
+                                          float(tau), float(phi), int(patience), int(probe_dim), _ptr(workspace),
+                                          ws_bytes, _ptr(out), _ptr(stop_pos), _ptr(blocks_fetched), _stream(dev))
+    _check(st, "attn_decode_art_list_ws")
     return out, stop_pos, blocks_fetched
 
 
@@ -695,4 +730,26 @@ def attn_decode_art_paged(q, k_pool, v_pool, block_table, seq_lens=None, order=N
                                         float(tau), float(phi), int(patience), int(probe_dim), _ptr(out),
                                         _ptr(stop_pos), _ptr(blocks_fetched), _stream(dev))
     _check(st, "attn_decode_art_paged")
+    return out, stop_pos, blocks_fetched
+
+
+def attn_decode_art_paged_ws(q, k_pool, v_pool, block_table, seq_lens=None, order=None, tau=1e-3, phi=1e-4,
+                             patience=2, probe_dim=8, scale=None, workspace=None, out=None, stop_pos=None,
+                             blocks_fetched=None):
+    """attn_decode_art_paged that may spread each (b, kv head) over several CUs through `workspace`."""
+    dev = q.device
+    dims, kv = _paged_dims(q, k_pool, v_pool, block_table, scale)
+    seq = _seq(seq_lens, dims.batch, dev)
+    if order is not None:
+        _need(order, "order", dev, torch.int32, (dims.batch, dims.num_kv_heads, dims.max_blocks))
+    workspace, ws_bytes = _art_workspace(dims, workspace, dev)
+    out = _out(out, (dims.batch, dims.num_q_heads, dims.head_dim), torch.float32, dev, "out")
+    stop_pos = _out(stop_pos, (dims.batch, dims.num_q_heads), torch.int32, dev, "stop_pos")
+    blocks_fetched = _out(blocks_fetched, (dims.batch, dims.num_kv_heads), torch.int32, dev, "blocks_fetched")
+    with _on_device(dev):
+        st = lib().attn_decode_art_paged_ws(ctypes.byref(dims), _ptr(q), ctypes.byref(kv), _ptr(seq),
+                                           _ptr(order), float(tau), float(phi), int(patience), int(probe_dim),
+                                           _ptr(workspace), ws_bytes, _ptr(out), _ptr(stop_pos),
+                                           _ptr(blocks_fetched), _stream(dev))
+    _check(st, "attn_decode_art_paged_ws")
     return out, stop_pos, blocks_fetched

@@ -369,17 +369,51 @@ size_t attn_art_workspace_bytes(const attn_dims* dims) {
   return skv::art_workspace_bytes((int32_t)units, dims->num_q_heads / dims->num_kv_heads, dims->head_dim);
 }
 
+// The workspace an ART call across workgroups needs: null when none is
+// needed (the call then runs one workgroup per unit); *st non-zero on error.
+static void* art_workspace(const attn_dims* dims, void* workspace, size_t workspace_bytes, int* st) {
+  *st = check_dims(dims);
+  if (*st) return nullptr;
+  const size_t need = attn_art_workspace_bytes(dims);
+  if (need && !workspace) *st = ATTN_ERR_INVALID_ARG;
+  else if (workspace_bytes < need) *st = ATTN_ERR_WORKSPACE;
+  return need ? workspace : nullptr;
+}
+
 int attn_decode_art_ws(const attn_dims* dims, const void* q, const void* k, const void* v,
                        const int32_t* seq_lens, const int32_t* order, float tau, float phi,
                        int32_t patience, int32_t probe_dim, void* workspace, size_t workspace_bytes,
                        float* out, int32_t* stop_pos, int32_t* blocks_fetched, void* stream) {
-  int st = check_dims(dims);
+  int st;
+  void* ws = art_workspace(dims, workspace, workspace_bytes, &st);
   if (st) return st;
-  const size_t need = attn_art_workspace_bytes(dims);
-  if (need && !workspace) return ATTN_ERR_INVALID_ARG;
-  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   return art_common(dims, q, k, v, seq_lens, order, dims->max_blocks, nullptr, tau, phi, patience, probe_dim,
-                    out, stop_pos, blocks_fetched, stream, nullptr, need ? workspace : nullptr, workspace_bytes);
+                    out, stop_pos, blocks_fetched, stream, nullptr, ws, workspace_bytes);
+}
+
+int attn_decode_art_list_ws(const attn_dims* dims, const void* q, const void* k, const void* v,
+                            const int32_t* seq_lens, const int32_t* block_list, const int32_t* n_list,
+                            int32_t max_list, float tau, float phi, int32_t patience, int32_t probe_dim,
+                            void* workspace, size_t workspace_bytes, float* out, int32_t* stop_pos,
+                            int32_t* blocks_fetched, void* stream) {
+  int st;
+  void* ws = art_workspace(dims, workspace, workspace_bytes, &st);
+  if (st) return st;
+  if (!block_list || !n_list || max_list < 1) return ATTN_ERR_INVALID_ARG;
+  return art_common(dims, q, k, v, seq_lens, block_list, max_list, n_list, tau, phi, patience, probe_dim, out,
+                    stop_pos, blocks_fetched, stream, nullptr, ws, workspace_bytes);
+}
+
+int attn_decode_art_paged_ws(const attn_dims* dims, const void* q, const attn_paged_kv* kv,
+                             const int32_t* seq_lens, const int32_t* order, float tau, float phi,
+                             int32_t patience, int32_t probe_dim, void* workspace, size_t workspace_bytes,
+                             float* out, int32_t* stop_pos, int32_t* blocks_fetched, void* stream) {
+  int st;
+  void* ws = art_workspace(dims, workspace, workspace_bytes, &st);
+  if (st) return st;
+  if ((st = check_paged(dims, kv, true))) return st;
+  return art_common(dims, q, kv->k_pool, kv->v_pool, seq_lens, order, dims->max_blocks, nullptr, tau, phi,
+                    patience, probe_dim, out, stop_pos, blocks_fetched, stream, kv, ws, workspace_bytes);
 }
 
 int attn_decode_art_list(const attn_dims* dims, const void* q, const void* k, const void* v,

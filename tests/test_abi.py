@@ -191,6 +191,18 @@ def test_art_workspace_and_validation(skv):
                                   FAKE, FAKE, None, None) == -1  # the attn_decode_art checks still apply
     assert call(None, 0, dims(head_dim=96)) == -2
     assert call(None, 0, dims(batch=0)) == 0  # nothing to do, nothing needed
+    # the list and paged twins check the workspace the same way, then their own arguments
+    lst = (FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 1e-3, 1e-4, 2, 8)
+    assert lib.attn_decode_art_list_ws(ctypes.byref(d), *lst, None, need, FAKE, FAKE, None, None) == -1
+    assert lib.attn_decode_art_list_ws(ctypes.byref(d), *lst, FAKE, need - 1, FAKE, FAKE, None, None) == -4
+    assert lib.attn_decode_art_list_ws(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, 4, 1e-3, 1e-4, 2, 8,
+                                       FAKE, need, FAKE, FAKE, None, None) == -1  # no block list
+    from sparse_kv_amd import AttnPagedKV
+
+    kv = AttnPagedKV(k_pool=0x1000, v_pool=None, pool_blocks=8, block_table=0x1000, table_stride=4)
+    pg = (FAKE, ctypes.byref(kv), None, None, 1e-3, 1e-4, 2, 8)
+    assert lib.attn_decode_art_paged_ws(ctypes.byref(d), *pg, FAKE, need - 1, FAKE, FAKE, None, None) == -4
+    assert lib.attn_decode_art_paged_ws(ctypes.byref(d), *pg, FAKE, need, FAKE, FAKE, None, None) == -1  # no v pool
 
 
 def test_status_strings(skv):

@@ -124,11 +124,16 @@ def test_importance_first_art_end_to_end(label, B, Hq, Hkv, d, L, seq, kind):
     assert_close(out.cpu().numpy(), ref_out, TOL, "importance-first ART output")
 
 
-def test_art_over_selected_lists():
-    """attn_decode_art_list on the oracle's top-k lists; unlisted blocks hold NaN."""
+def art_list(path):
     import sparse_kv_amd as skv
 
-    log("[order] ART over top-k lists (sink first, ascending)")
+    return skv.attn_decode_art_list_ws if path == "ws" else skv.attn_decode_art_list
+
+
+@pytest.mark.parametrize("path", ["one", "ws"])
+def test_art_over_selected_lists(path):
+    """attn_decode_art_list[_ws] on the oracle's top-k lists; unlisted blocks hold NaN."""
+    log(f"[order] ART over top-k lists (sink first, ascending), {path}")
     B, Hq, Hkv, d, L = 2, 8, 2, 128, 64 * 48
     seq = [64 * 48, 64 * 31 + 20]
     inp = synth.make_inputs(61, B, Hq, Hkv, d, L, kind="recency", seq_lens=seq, recent_tokens=64 * 5)
@@ -152,8 +157,8 @@ def test_art_over_selected_lists():
         poisoned = synth.DecodeInputs(inp.q, inp.k.copy(), inp.v.copy(), inp.seq_lens, inp.dtype)
         synth.poison_blocks(poisoned, lists)
         q, k, v, sl = upload(poisoned)
-        out, stop, fetched = skv.attn_decode_art_list(q, k, v, dev_i32(bl), dev_i32(nl), sl, tau=tau, phi=phi,
-                                                      patience=p, probe_dim=PROBE)
+        out, stop, fetched = art_list(path)(q, k, v, dev_i32(bl), dev_i32(nl), sl, tau=tau, phi=phi,
+                                            patience=p, probe_dim=PROBE)
         torch.cuda.synchronize()
         stop, fetched = stop.cpu().numpy(), fetched.cpu().numpy()
         log(f"  tau={tau}: stops {stop.ravel().tolist()}")
@@ -167,19 +172,18 @@ def test_art_over_selected_lists():
             assert_close(out.cpu().numpy(), dense_lists, TOL, "tau = 0 equals attention over the lists")
 
 
-def test_art_list_edge_counts():
+@pytest.mark.parametrize("path", ["one", "ws"])
+def test_art_list_edge_counts(path):
     """n_list = 0, n_list past the sequence and past max_list, ragged rows."""
-    import sparse_kv_amd as skv
-
-    log("[order] ART list edge counts")
+    log(f"[order] ART list edge counts, {path}")
     B, Hq, Hkv, d, L = 3, 4, 1, 128, 64 * 10
     inp = synth.make_inputs(62, B, Hq, Hkv, d, L, kind="gauss", seq_lens=[64 * 10, 64 * 3 + 1, 64 * 10])
     max_list = 6
     bl = np.array([[[0, 9, 2, 5, 7, 1]], [[0, 3, 1, 2, -1, -1]], [[0, 4, 8, 3, 6, 2]]], dtype=np.int32)
     nl = np.array([[0], [9], [100]], dtype=np.int32)  # 0 -> nothing; 9 -> nb = 4; 100 -> max_list = 6
     q, k, v, sl = upload(inp)
-    out, stop, fetched = skv.attn_decode_art_list(q, k, v, dev_i32(bl), dev_i32(nl), sl, tau=0.0, phi=0.0,
-                                                  patience=1, probe_dim=PROBE)
+    out, stop, fetched = art_list(path)(q, k, v, dev_i32(bl), dev_i32(nl), sl, tau=0.0, phi=0.0, patience=1,
+                                        probe_dim=PROBE)
     torch.cuda.synchronize()
     out, stop, fetched = out.cpu().numpy(), stop.cpu().numpy(), fetched.cpu().numpy()
     assert stop[0].tolist() == [-1] * Hq and not out[0].any() and fetched[0, 0] == 0

@@ -127,17 +127,18 @@ def test_centroids_paged():
     assert_close(C.cpu().numpy(), ref, 1e-5, "paged centroids built then updated")
 
 
-def test_art_paged():
+@pytest.mark.parametrize("path", ["one", "ws"])
+def test_art_paged(path):
     import sparse_kv_amd as skv
     from tests.test_gpu_art import P, PHI, PROBE, TAU, art_inputs
 
-    log("[paged] ART stop positions")
+    log(f"[paged] ART stop positions, {path}")
     inp, ref_out, ref_stop = art_inputs(73, 2, 8, 2, 128, 64 * 40, seq=[64 * 40, 64 * 33 + 9])
     kp, vp, table = make_pool(inp, 4)
     q, k, v, sl = upload(inp)
     kpd, vpd, tab = up_pool(kp, vp, table, "bf16")
-    out, stop, fetched = skv.attn_decode_art_paged(q, kpd, vpd, tab, sl, tau=TAU, phi=PHI, patience=P,
-                                                   probe_dim=PROBE)
+    fn = skv.attn_decode_art_paged_ws if path == "ws" else skv.attn_decode_art_paged
+    out, stop, fetched = fn(q, kpd, vpd, tab, sl, tau=TAU, phi=PHI, patience=P, probe_dim=PROBE)
     torch.cuda.synchronize()
     assert np.array_equal(stop.cpu().numpy(), ref_stop)
     assert_close(out.cpu().numpy(), ref_out, TOL, "paged ART output")
