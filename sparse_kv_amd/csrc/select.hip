@@ -185,6 +185,41 @@ __device__ int block_exscan(int x, int* total, int* lds4) {
   return base + inc - x;
 }
 
+// Exclusive prefix sums of two ints per thread in one pass (same barriers
+// as one): returns a's prefix, writes b's prefix and both totals.
+__device__ int block_exscan2(int a, int b, int* tot_a, int* tot_b, int* pre_b) {
+  __shared__ int lds[2][4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int ia = a, ib = b;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ya = __shfl_up(ia, off), yb = __shfl_up(ib, off);
+    if (lane >= off) {
+      ia += ya;
+      ib += yb;
+    }
+  }
+  if (lane == 63) {
+    lds[0][w] = ia;
+    lds[1][w] = ib;
+  }
+  __syncthreads();
+  int ba = 0, bb = 0, ta = 0, tb = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int va = lds[0][i], vb = lds[1][i];
+    ba += i < w ? va : 0;
+    bb += i < w ? vb : 0;
+    ta += va;
+    tb += vb;
+  }
+  __syncthreads();
+  *tot_a = ta;
+  *tot_b = tb;
+  *pre_b = bb + ib - b;
+  return ba + ia - a;
+}
+
 // Radix select (8 bits a pass, 256-thread workgroup) of the kk-th largest
 // key among items [0, n) with elig(i): returns that key and how many items
 // equal to it are to be taken (lowest indices first).  0 < kk < #eligible.
@@ -222,31 +257,110 @@ __device__ void radix_select(int n, int kk, KeyF key, EligF elig, uint32_t* hist
   need_eq = rem;
 }
 
+// The kk-th largest key in one histogram pass, for keys cheap to read twice
+// (staged in LDS): a 4096-bin histogram of the top 12 key bits locates the
+// bin holding it (thread t sums bins 4095 - 16t ...; one block scan), then
+// that bin's keys are ranked against each other.  False -- nothing decided
+// -- when that bin holds more than 256 keys (heavy ties or clustering).
+template <typename KeyF, typename EligF>
+__device__ bool select_wide(int n, int kk, KeyF key, EligF elig, uint32_t* hist, uint32_t* cand, int* scan4,
+                            uint32_t* sh_prefix, int* sh_rem, uint32_t& thr, int& need_eq) {
+  __shared__ int sh[4];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 4096; i += 256) hist[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 256)
+    if (elig(i)) atomicAdd(&hist[key(i) >> 20], 1u);
+  __syncthreads();
+  int loc = 0;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) loc += (int)hist[4095 - 16 * tid - c];
+  int tot;
+  const int above = block_exscan(loc, &tot, scan4);  // keys in the bins above this thread's
+  if (above < kk && kk <= above + loc) {
+    int a = above;
+    for (int c = 0; c < 16; ++c) {
+      const int bin = 4095 - 16 * tid - c;
+      const int h = (int)hist[bin];
+      if (a + h >= kk) {
+        sh[0] = bin;
+        sh[1] = kk - a;  // how many of the bin's keys are among the kk
+        sh[2] = h;
+        break;
+      }
+      a += h;
+    }
+  }
+  if (tid == 0) sh[3] = 0;
+  __syncthreads();
+  const uint32_t bin = (uint32_t)sh[0];
+  const int rem = sh[1], cnt = sh[2];
+  if (cnt > 256) return false;
+  for (int i = tid; i < n; i += 256)
+    if (elig(i) && (key(i) >> 20) == bin) cand[atomicAdd(&sh[3], 1)] = key(i);
+  __syncthreads();
+  if (tid < cnt) {
+    const uint32_t x = cand[tid];
+    int gt = 0, ge = 0;
+    for (int c = 0; c < cnt; ++c) {
+      gt += cand[c] > x ? 1 : 0;
+      ge += cand[c] >= x ? 1 : 0;
+    }
+    if (gt < rem && rem <= ge) {  // x is the rem-th largest of the bin (equal keys write equal values)
+      *sh_prefix = x;
+      *sh_rem = rem - gt;
+    }
+  }
+  __syncthreads();
+  thr = *sh_prefix;
+  need_eq = *sh_rem;
+  __syncthreads();
+  return true;
+}
+
 // Calls take(i, rank) for the kk best eligible items of [0, n) in index
 // order (rank = 0, 1, ... over the taken items), ties to the lower index.
 // Each thread owns a contiguous chunk, so ranks follow the index order.
 // Returns the number taken.
-template <typename KeyF, typename EligF, typename TakeF>
+// With WIDE, hist holds 4096 entries and cand 256, and the threshold comes
+// from select_wide when it can decide.  ALL: every item is eligible.
+template <bool WIDE = false, bool ALL = false, typename KeyF, typename EligF, typename TakeF>
 __device__ int take_best(int n, int kk, KeyF key, EligF elig, TakeF take, uint32_t* hist, int* scan4,
-                         uint32_t* sh_prefix, int* sh_rem) {
+                         uint32_t* sh_prefix, int* sh_rem, uint32_t* cand = nullptr) {
   const int tid = threadIdx.x;
   const int CH = (n + 255) / 256;
   const int i0 = min(tid * CH, n), i1 = min(i0 + CH, n);
-  int ne = 0;
-  for (int i = i0; i < i1; ++i) ne += elig(i) ? 1 : 0;
-  int n_elig;
-  block_exscan(ne, &n_elig, scan4);
+  int n_elig = n;
+  if constexpr (!ALL) {
+    int ne = 0;
+    for (int i = i0; i < i1; ++i) ne += elig(i) ? 1 : 0;
+    block_exscan(ne, &n_elig, scan4);
+  }
   const int kq = min(kk, n_elig);
   const bool ranked = kq > 0 && kq < n_elig;
   uint32_t thr = 0;
   int need_eq = 0;
-  if (ranked) radix_select(n, kq, key, elig, hist, scan4, sh_prefix, sh_rem, thr, need_eq);
-  int eq_local = 0;
-  if (ranked)
-    for (int i = i0; i < i1; ++i)
-      if (elig(i) && key(i) == thr) ++eq_local;
-  int tot_eq;
-  const int eq_before = block_exscan(eq_local, &tot_eq, scan4);
+  if (ranked) {
+    bool done = false;
+    if constexpr (WIDE) done = select_wide(n, kq, key, elig, hist, cand, scan4, sh_prefix, sh_rem, thr, need_eq);
+    if (!done) radix_select(n, kq, key, elig, hist, scan4, sh_prefix, sh_rem, thr, need_eq);
+  }
+  // per chunk: keys equal to the threshold and keys above it (every
+  // eligible key when nothing is ranked); the items chosen before a chunk
+  // are the keys above before it plus its share of the first need_eq ties
+  int eq_local = 0, gt_local = 0;
+  for (int i = i0; i < i1; ++i) {
+    if (!elig(i)) continue;
+    if (!ranked) {
+      ++gt_local;
+    } else {
+      const uint32_t u = key(i);
+      gt_local += u > thr ? 1 : 0;
+      eq_local += u == thr ? 1 : 0;
+    }
+  }
+  int eq_tot, gt_tot, gt_before;
+  const int eq_before = block_exscan2(eq_local, gt_local, &eq_tot, &gt_tot, &gt_before);
   auto chosen = [&](int i, int& eq_seen) -> bool {
     if (kq == 0 || !elig(i)) return false;
     if (!ranked) return true;
@@ -255,11 +369,9 @@ __device__ int take_best(int n, int kk, KeyF key, EligF elig, TakeF take, uint32
     if (u == thr) return eq_seen++ < need_eq;
     return false;
   };
-  int eq_seen = eq_before, cnt = 0;
-  for (int i = i0; i < i1; ++i) cnt += chosen(i, eq_seen) ? 1 : 0;
-  int total;
-  int rank = block_exscan(cnt, &total, scan4);
-  eq_seen = eq_before;
+  int rank = kq == 0 ? 0 : (ranked ? gt_before + min(eq_before, need_eq) : gt_before);
+  const int total = kq == 0 ? 0 : (ranked ? gt_tot + need_eq : gt_tot);
+  int eq_seen = eq_before;
   for (int i = i0; i < i1; ++i)
     if (chosen(i, eq_seen)) take(i, rank++);
   __syncthreads();
@@ -276,7 +388,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
                                                    int32_t n_recent, int32_t max_sel, int32_t* __restrict__ idx,
                                                    int32_t* __restrict__ n_sel) {
   __shared__ uint32_t keys[kTopkStage];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t cand[256];
   __shared__ int scan4[4];
   __shared__ uint32_t sh_prefix;
   __shared__ int sh_rem;
@@ -295,12 +408,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
     for (int i = tid; i < ncand; i += 256) keys[i] = score_key(row[sink_hi + i]);
   __syncthreads();
   auto key = [&](int i) { return staged ? keys[i] : score_key(row[sink_hi + i]); };
-  const int npick = take_best(
-      ncand, k, key, [](int) { return true; },
-      [&](int i, int r) {
-        if (sink_hi + r < max_sel) out[sink_hi + r] = sink_hi + i;
-      },
-      hist, scan4, &sh_prefix, &sh_rem);
+  auto put = [&](int i, int r) {
+    if (sink_hi + r < max_sel) out[sink_hi + r] = sink_hi + i;
+  };
+  auto all = [](int) { return true; };
+  // staged keys are cheap to read twice: one histogram pass usually decides
+  const int npick = staged ? take_best<true, true>(ncand, k, key, all, put, hist, scan4, &sh_prefix, &sh_rem, cand)
+                           : take_best<false, true>(ncand, k, key, all, put, hist, scan4, &sh_prefix, &sh_rem);
   for (int j = tid; j < sink_hi; j += 256)
     if (j < max_sel) out[j] = j;
   for (int j = rec_lo + tid; j < nb; j += 256) {
