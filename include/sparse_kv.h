@@ -291,7 +291,7 @@ int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const v
  * B * Hkv <= 128 and at least 2 CUs per (b, kv head) on the current device,
  * each (b, kv head) is streamed by up to 4 workgroups on different CUs that
  * hand block states to per-head folding waves through the workspace;
- * read-ahead past the stop is then at most max(32, T + 1) blocks, and at
+ * read-ahead past the stop is then at most max(64, T + 1) blocks, and at
  * most 128, per KV head.  Otherwise it runs as attn_decode_art and the
  * workspace is not touched.
  *   workspace        device memory of at least attn_art_workspace_bytes(dims)

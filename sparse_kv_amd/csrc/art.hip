@@ -69,10 +69,11 @@ struct ArtWaves {
 // folder has finished.
 constexpr int kDoneMark = 1 << 30;
 // Read-ahead allowed once f positions are folded: the ring size, but no more
-// than max(32, f), so a head that stops early wastes few blocks.
+// than max(64, f), so a head that stops early wastes few blocks (a 32-block
+// floor held the producers back while the first positions were folded).
 template <int R>
 __device__ __forceinline__ int window_span(int f) {
-  return min(R, max(32, f));
+  return min(R, max(64, f));
 }
 
 // In LDS: one workgroup per (b, kv head).  Acquire/release on LDS words.
@@ -105,6 +106,8 @@ struct LdsRing {
   __device__ float l_at(int s, int q) { return l[s][q]; }
   static constexpr int kMaxBatch = R;
   __device__ int window() { return ld_acq(&folded); }
+  __device__ int window_load() { return ld_acq(&folded); }
+  static __device__ int window_of(int v) { return v; }
   __device__ void set_folded(int, int v) { st_rel(&folded, v); }
   template <int FE>
   __device__ void acc_row(int s, int q, int col, float (&x)[FE]) {
@@ -193,10 +196,12 @@ struct GlobalRing {
     asm volatile("" ::: "memory");
   }
   // the least count of folded positions over the folders (kDoneMark: all done)
-  __device__ int window() {
+  __device__ int window_load() {
     const int lane = threadIdx.x & 63;
-    int v = lane < NF ? __hip_atomic_load(&ctrl[kFolded + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                      : kDoneMark;
+    return lane < NF ? __hip_atomic_load(&ctrl[kFolded + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kDoneMark;
+  }
+  __device__ int window() { return window_of(window_load()); }
+  static __device__ int window_of(int v) {
     v = min(v, __shfl_xor(v, 1));
     v = min(v, __shfl_xor(v, 2));
     v = min(v, __shfl_xor(v, 4));
@@ -320,15 +325,17 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, RING& ring, POS& pos, int
   };
   auto block_from = [&](int t, int o) { return p.order ? clampi(o, 0, nb - 1) : (t == 0 ? 0 : nb - t); };
   // read-ahead window: position t may start once the folders are within
-  // window_span of it; false once they have finished.  It is read afresh
-  // for every block: a look per block keeps read-ahead (and over-fetch past
-  // the stop) in check and shows at once that the folders have finished.
-  auto window_wait = [&](int t) {
+  // window_span of it (f: a count of folded positions read earlier); false
+  // once they have finished.  A fresh count is read for every block, while
+  // that block's state stores complete: a look per block keeps read-ahead
+  // (and over-fetch past the stop) in check and shows soon after that the
+  // folders have finished.
+  auto window_wait = [&](int t, int f) {
     while (true) {
-      const int f = ring.window();
       if (f >= kDoneMark) return false;
       if (f > t - window_span<kR>(f)) return true;
       __builtin_amdgcn_s_sleep(1);
+      f = ring.window();
     }
   };
   u32x4 kr[4][KA], vr[CPR];
@@ -378,7 +385,7 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, RING& ring, POS& pos, int
   };
 
   int t = pos.first();
-  if (t >= nv || !window_wait(t)) return;
+  if (t >= nv || !window_wait(t, ring.window())) return;
   int j = block_from(t, order_at(t));
   {
     const uint32_t so = block_off(j);
@@ -476,9 +483,10 @@ __device__ void art_producer(const ArtArgs& p, SH& sh, RING& ring, POS& pos, int
 #pragma unroll
       for (int r = 0; r < GR; ++r) ring.put_ml(s, 4 * r + kg, mb[r], lb[r]);
     }
+    const int wv = ring.window_load();  // read while the state stores complete
     ring.publish(s, t, lane);
 
-    if (tn >= nv || !window_wait(tn)) return;
+    if (tn >= nv || !window_wait(tn, RING::window_of(wv))) return;
     j = block_from(tn, onext);
     const uint32_t so = block_off(j);
     load_k(so);

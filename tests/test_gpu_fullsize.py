@@ -160,7 +160,7 @@ def test_art_128k_batch8_across_workgroups():
         assert stop1[b, g * G:(g + 1) * G].tolist() == rs[0].tolist(), f"one-workgroup stops of unit ({b},{g})"
         assert_close(out[b, g * G:(g + 1) * G], ro[0], TOL, f"ART unit ({b},{g})")
         need = int(rs.max()) + 1
-        assert need <= fetched[b, g] <= need + 128, (b, g, need, fetched[b, g])
+        assert need <= fetched[b, g] <= need + min(128, max(64, need)), (b, g, need, fetched[b, g])
         checked += 1
         if checked == 3:
             break
