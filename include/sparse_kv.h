@@ -97,6 +97,7 @@ int attn_decode_dense(const attn_dims* dims, const void* q, const void* k, const
  *   out     float [rows, head_dim]   (all states empty: zeros)
  *   m_out, l_out  float [rows] or NULL: the merged state (M, sum_r w_r);
  *                 (-inf, 0) when every state is empty.
+ * A state with l_r = 0 is empty: its m_r and o_r never reach the result.
  * Requires rows >= 0, S >= 1, head_dim in {64, 128}.
  */
 int attn_merge_states(int32_t rows, int32_t num_splits, int32_t head_dim, const float* m,

@@ -11,81 +11,108 @@
 namespace skv {
 namespace {
 
-// One workgroup (4 wave64s) per output row.  Wave w takes the splits
-// s = w, w + 4, ...; within a wave the lanes first hold one split each (max
-// and weights, staged in LDS), then d/64 channels each while the split
-// outputs are accumulated.  The 4 partial sums meet in LDS.
+// One wave64 per output row, four rows per workgroup.  Lane i holds channels
+// i * d/64 .. of the output.  The first kChunk split outputs of the row are
+// loaded together with the split states, so a merge of up to kChunk splits
+// costs one round trip to memory; further splits follow kChunk at a time.
+// A state with l = 0 is empty: it never touches the sums, whatever its o.
+constexpr int kChunk = 16;
+
+template <int PER>
+__device__ __forceinline__ void load_row_part(const float* src, float (&x)[PER]) {
+  if constexpr (PER == 2) {
+    const float2 v = *(const float2*)src;
+    x[0] = v.x;
+    x[1] = v.y;
+  } else {
+    x[0] = src[0];
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(int32_t rows, int32_t S, const float* __restrict__ m,
                                                     const float* __restrict__ l, const float* __restrict__ o,
                                                     float* __restrict__ out, float* __restrict__ m_out,
                                                     float* __restrict__ l_out) {
   constexpr int PER = D / 64;
-  constexpr int NW = 4;
-  __shared__ float red[NW][D];
-  __shared__ float red_w[NW], red_m[NW];
-  __shared__ float wts[NW][64];
-  const int row = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (row >= rows) return;
   const float* mr = m + (size_t)row * S;
   const float* lr = l + (size_t)row * S;
+  const float* orow = o + (size_t)row * S * D + lane * PER;
 
-  // global max over the non-empty splits
-  float mx = -INFINITY;
-  for (int s = w + NW * lane; s < S; s += NW * 64)
+  // the first chunk of split outputs, in flight with the states
+  float x[kChunk][PER];
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) {
+    if (i < S) {
+      load_row_part<PER>(orow + (size_t)i * D, x[i]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) x[i][k] = 0.f;
+    }
+  }
+  // states of splits lane, lane + 64, ...: the first 64 stay in registers
+  const float m0 = lane < S ? mr[lane] : -INFINITY;
+  const float l0 = lane < S ? lr[lane] : 0.f;
+  float mx = l0 > 0.f ? m0 : -INFINITY;
+  for (int s = lane + 64; s < S; s += 64)
     if (lr[s] > 0.f) mx = fmaxf(mx, mr[s]);
-  mx = wave_max(mx);
-  if (lane == 0) red_m[w] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  const float M = wave_max(mx);
 
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
   float wsum = 0.f;
   if (M != -INFINITY) {
-    for (int s0 = w; s0 < S; s0 += NW * 64) {
-      // lane i holds the weight of split s0 + NW * i
-      const int s = s0 + NW * lane;
-      float wt = 0.f;
-      if (s < S) {
-        const float ls = lr[s];
-        wt = ls > 0.f ? ls * fast_exp2((mr[s] - M) * kLog2e) : 0.f;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      float ls = l0, ms = m0;
+      if (s0 > 0) {
+        const int s = s0 + lane;
+        ls = s < S ? lr[s] : 0.f;
+        ms = s < S ? mr[s] : -INFINITY;
       }
+      // lane i holds the weight of split s0 + i
+      const float wt = ls > 0.f ? ls * fast_exp2((ms - M) * kLog2e) : 0.f;
       wsum += wt;
-      wts[w][lane] = wt;  // read back by the same wave only
-      const int n = min(64, (S - s0 + NW - 1) / NW);
-      const float* ob = o + ((size_t)row * S + s0) * D + lane * PER;
-#pragma unroll 8
-      for (int i = 0; i < n; ++i) {
-        const float f = wts[w][i];
-        const float* os = ob + (size_t)NW * i * D;
+      const int n = min(64, S - s0);
+      for (int c = 0; c < n; c += kChunk) {
+        float y[kChunk][PER];
+        if (s0 + c == 0) {
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          const float x = os[k];
-          acc[k] = f != 0.f ? fmaf(f, x, acc[k]) : acc[k];  // empty splits never touch acc
+          for (int i = 0; i < kChunk; ++i)
+#pragma unroll
+            for (int k = 0; k < PER; ++k) y[i][k] = x[i][k];
+        } else {
+#pragma unroll
+          for (int i = 0; i < kChunk; ++i) {
+            if (c + i < n) {
+              load_row_part<PER>(orow + (size_t)(s0 + c + i) * D, y[i]);
+            } else {
+#pragma unroll
+              for (int k = 0; k < PER; ++k) y[i][k] = 0.f;
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+          if (c + i < n) {
+            const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), c + i));
+#pragma unroll
+            for (int k = 0; k < PER; ++k) acc[k] = f != 0.f ? fmaf(f, y[i][k], acc[k]) : acc[k];
+          }
         }
       }
     }
   }
-  wsum = wave_sum(wsum);
+  const float L = wave_sum(wsum);
+  float* dst = out + (size_t)row * D + lane * PER;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) red[w][lane * PER + k] = acc[k];
-  if (lane == 0) red_w[w] = wsum;
-  __syncthreads();
-  if (w == 0) {
-    const float L = red_w[0] + red_w[1] + red_w[2] + red_w[3];
-    float* dst = out + (size_t)row * D + lane * PER;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int c = lane * PER + k;
-      const float a = red[0][c] + red[1][c] + red[2][c] + red[3][c];
-      dst[k] = L > 0.f ? a / L : 0.f;
-    }
-    if (lane == 0) {
-      if (m_out) m_out[row] = L > 0.f ? M : -INFINITY;
-      if (l_out) l_out[row] = L;
-    }
+  for (int k = 0; k < PER; ++k) dst[k] = L > 0.f ? acc[k] / L : 0.f;
+  if (lane == 0) {
+    if (m_out) m_out[row] = L > 0.f ? M : -INFINITY;
+    if (l_out) l_out[row] = L;
   }
 }
 
@@ -94,7 +121,7 @@ __global__ __launch_bounds__(256) void merge_kernel(int32_t rows, int32_t S, con
 hipError_t launch_merge(int32_t rows, int32_t S, int32_t d, const float* m, const float* l,
                         const float* o, float* out, float* m_out, float* l_out, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  const dim3 grid(rows);
+  const dim3 grid((rows + 3) / 4);
   if (d == 128)
     merge_kernel<128><<<grid, 256, 0, st>>>(rows, S, m, l, o, out, m_out, l_out);
   else

@@ -68,10 +68,12 @@ def test_block_range_and_determinism():
     assert_states_close(m, l, o, rm, rl, ro, TOL, "range states")
 
 
-def test_merge_random_states():
-    log("[merge] random states with empty entries")
-    r = np.random.default_rng(5)
-    rows, S, d = 37, 7, 128
+@pytest.mark.parametrize("S", [1, 7, 16, 17, 64, 100])
+def test_merge_random_states(S):
+    # one split, the first output chunk (16 splits) and past it, one and two rounds of 64 states
+    log(f"[merge] random states with empty entries, S={S}")
+    r = np.random.default_rng(5 + S)
+    rows, d = 37, 128
     m = r.standard_normal((rows, S)) * 4
     l = np.exp(r.standard_normal((rows, S)))
     o = r.standard_normal((rows, S, d))
@@ -88,6 +90,12 @@ def test_merge_random_states():
                                                      o.astype(np.float32).astype(np.float64))
     assert_close(out.cpu().numpy(), RO, 1e-5, "merge output")
     assert np.isneginf(mo.cpu().numpy()[3]) and lo.cpu().numpy()[3] == 0 and not out[3].any()
+    # an empty state's output is never used: NaN there changes nothing
+    on = o.copy()
+    on[empty] = np.nan
+    outn = skv.attn_merge_states(t(m), t(l), t(on))
+    torch.cuda.synchronize()
+    assert torch.equal(outn, out), "NaN in an empty state's output reached the merge"
     for dd in (64,):
         o64 = o[..., :dd].copy()
         out64 = skv.attn_merge_states(t(m), t(l), t(o64))
