@@ -447,10 +447,11 @@ __global__ __launch_bounds__(1024) void order_kernel(const float* __restrict__ s
   for (int i = tid; i < n; i += 1024)
     key[i] = i < nr ? ((uint64_t)~score_key(row[i + 1]) << 32) | (uint32_t)(i + 1) : ~(uint64_t)0;
   __syncthreads();
-  for (int kk = 2; kk <= n; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
+  for (int kk = 2, lk = 1; kk <= n; kk <<= 1, ++lk) {
+    for (int j = kk >> 1, lj = lk - 1; j > 0; j >>= 1, --lj) {
       for (int pr = tid; pr < (n >> 1); pr += 1024) {
-        const int i = 2 * j * (pr / j) + pr % j;  // pair (i, i + j)
+        // pair (i, i + j) with i = 2 j floor(pr / j) + pr mod j; j = 2^lj
+        const int i = ((pr >> lj) << (lj + 1)) | (pr & (j - 1));
         const uint64_t x = key[i], y = key[i + j];
         const bool up = (i & kk) == 0;
         if ((x > y) == up) {
