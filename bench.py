@@ -200,12 +200,16 @@ def main():
     names = ["dense_kernel", "dense_merge", "sparse", "art", "window"]
     ev = {}
 
+    ev_timed = {}
+
     def step(record):
+        # record: "all" (every stage boundary, into ev), "dense" (the dense
+        # kernel's two boundaries only, into ev_timed) or None
         def mark(tag):
-            if record:
+            if record == "all" or (record == "dense" and tag.startswith("dense_kernel")):
                 e = torch.cuda.Event(enable_timing=True)
                 e.record()
-                ev.setdefault(tag, []).append(e)
+                (ev if record == "all" else ev_timed).setdefault(tag, []).append(e)
 
         if "dense" in stages:
             kd, vd = copies["dense"]
@@ -263,23 +267,25 @@ def main():
             mark("art_imp.1")
 
     for _ in range(args.warmup):
-        step(False)
+        step(None)
     torch.cuda.synchronize()
-    # the timed steps carry no events (a stage-boundary event costs a few
-    # microseconds); a second pass of the same steps records the per-stage
-    # and dense-kernel events for the breakdown and the roofline
+    # the timed steps carry only the two events around the dense kernel (its
+    # launch duration for the roofline, on the stream it runs on); a second
+    # pass of the same steps records every stage boundary for the breakdown
+    # (a stage-boundary event costs a few microseconds)
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        step(False)
+        step("dense")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
     for _ in range(args.steps):
-        step(True)
+        step("all")
     torch.cuda.synchronize()
 
-    def avg_ms(a, b):
-        xs = [e0.elapsed_time(e1) for e0, e1 in zip(ev[a], ev[b])]
+    def avg_ms(a, b, evs=None):
+        evs = ev if evs is None else evs
+        xs = [e0.elapsed_time(e1) for e0, e1 in zip(evs[a], evs[b])]
         return sum(xs) / len(xs)
 
     # algorithmic bytes per stage
@@ -291,7 +297,7 @@ def main():
     total_bytes = 0.0
     gbs = lambda by, ms: by / (ms * 1e-3) / 1e9
     if "dense" in stages:
-        kern_ms = avg_ms("dense_kernel.0", "dense_kernel.1")
+        kern_ms = avg_ms("dense_kernel.0", "dense_kernel.1", ev_timed)  # inside the timed steps
         path_ms = avg_ms("dense_kernel.0", "dense_merge.1")
         by = units * NB * kv_block + q_bytes + o_bytes
         total_bytes += by
