@@ -28,6 +28,12 @@
 // waits for slot t%R to hold position t.  The folder is never blocked by a
 // producer that is itself blocked: the owner of the next position to fold
 // always has its slot free.  Producers leave when the folder signals done.
+//
+// With fewer (b, kv head) units than half the CUs, a second form spreads each
+// unit over up to 4 workgroups (art_mc_kernel below): the ring moves to a
+// caller-provided workspace in device memory (128 slots, device-scope
+// accesses), producers claim visit positions from a per-unit counter, and
+// one folder wave per query head folds batches of up to 64 positions.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
