@@ -1,0 +1,128 @@
+"""GPU parity at the size limits: a (b, kv head) K/V slice of exactly 2 GiB
+(131072 blocks of bf16 d 128, the largest the library accepts) and top-k rows
+longer than the candidates a workgroup stages in LDS.
+
+The 2 GiB slice is built on the device: zero keys and values except a few
+tokens, so the exact attention output has a closed form (softmax attention
+as defined in the "ART (Attention Run-time Termination)" summary, §2.1): with
+logits s_t, the output is sum_t e^{s_t} v_t / sum_t e^{s_t}, where every
+token with a zero key adds e^0 = 1 to the denominator and nothing to the
+numerator unless its value row is set."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import TOL, assert_close, log
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+NB = 131072  # 131072 blocks x 64 tokens x 256 bytes = 2 GiB per K (and V) slice
+N = NB * 64
+
+
+def bf16_round(x):
+    return float(torch.tensor([x], dtype=torch.float32).to(torch.bfloat16).float())
+
+
+def build_max_slice():
+    """Keys: zero except channel 0 of three tokens; values: zero except a few
+    rows.  Returns device q, k, v and the host description."""
+    scale = 1.0 / math.sqrt(D)
+    qv = 8.0
+    special = {0: 19.0, N // 2 + 37: 18.0, N - 1: 20.0}  # token -> target logit
+    key0 = {t: bf16_round(s / (scale * qv)) for t, s in special.items()}
+    r = np.random.default_rng(123)
+    vrows = sorted({0, 1, N // 2 + 37, N - 65, N - 2, N - 1})
+    vals = {t: r.standard_normal(D).astype(np.float32) for t in vrows}
+    q = torch.zeros(1, 1, D, dtype=torch.bfloat16, device="cuda")
+    q[0, 0, 0] = qv
+    k = torch.zeros(1, 1, N, D, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros(1, 1, N, D, dtype=torch.bfloat16, device="cuda")
+    for t, a in key0.items():
+        k[0, 0, t, 0] = a
+    for t, x in vals.items():
+        v[0, 0, t] = torch.from_numpy(x).to(torch.bfloat16)
+    vals = {t: v[0, 0, t].float().cpu().numpy().astype(np.float64) for t in vrows}  # the stored bf16 rows
+    return q, k, v, dict(scale=scale, qv=qv, key0=key0, vals=vals)
+
+
+def exact_output(desc, tokens_lo_hi):
+    """Closed-form attention over the token ranges [(lo, hi), ...]."""
+    n_tok = sum(hi - lo for lo, hi in tokens_lo_hi)
+    inside = lambda t: any(lo <= t < hi for lo, hi in tokens_lo_hi)
+    logits = {t: desc["scale"] * desc["qv"] * a for t, a in desc["key0"].items() if inside(t)}
+    M = max(list(logits.values()) + [0.0])
+    num = np.zeros(D)
+    den = (n_tok - len(logits)) * math.exp(-M)
+    for t, s in logits.items():
+        den += math.exp(s - M)
+    for t, x in desc["vals"].items():
+        if inside(t):
+            num += math.exp(logits.get(t, 0.0) - M) * x
+    return num / den
+
+
+@pytest.fixture(scope="module")
+def max_slice():
+    q, k, v, desc = build_max_slice()
+    torch.cuda.synchronize()
+    yield q, k, v, desc
+    del q, k, v
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("L", [N, N - 30, 64 * (NB // 2) + 1])
+def test_dense_decode_on_a_2gib_slice(max_slice, L):
+    import sparse_kv_amd as skv
+
+    q, k, v, desc = max_slice
+    log(f"[max] dense decode over a 2 GiB K/V slice, L={L}")
+    sl = torch.tensor([L], dtype=torch.int32, device="cuda")
+    want = exact_output(desc, [(0, L)])
+    for S in (1, 4, 64):
+        out = skv.attn_merge_states(*skv.attn_decode_dense(q, k, v, sl, num_splits=S))
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy()[0, 0], want, TOL, f"L={L} S={S}")
+
+
+def test_listed_decode_on_a_2gib_slice(max_slice):
+    import sparse_kv_amd as skv
+
+    q, k, v, desc = max_slice
+    log("[max] listed-block decode over blocks 0, the middle one and the last of a 2 GiB slice")
+    blocks = [0, (N // 2 + 37) // 64, NB - 1]
+    idx = torch.tensor([[blocks]], dtype=torch.int32, device="cuda")
+    n = torch.tensor([[len(blocks)]], dtype=torch.int32, device="cuda")
+    want = exact_output(desc, [(64 * j, 64 * j + 64) for j in blocks])
+    for S in (1, 3):
+        out = skv.attn_merge_states(*skv.attn_decode_sparse(q, k, v, idx, n, None, num_splits=S))
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy()[0, 0], want, TOL, f"listed S={S}")
+
+
+@pytest.mark.parametrize("NBr", [20000, 40001])
+def test_topk_rows_longer_than_the_staged_keys(NBr):
+    # more candidates than the 16384 keys a workgroup stages: every select pass reads memory
+    import sparse_kv_amd as skv
+
+    log(f"[max] top-k on {NBr}-block rows")
+    r = np.random.default_rng(NBr)
+    B, Hkv = 1, 2
+    s = (r.standard_normal((B, Hkv, NBr)) * 2).astype(np.float32)
+    s[0, 1] = np.round(s[0, 1] * 8) / 8  # heavy ties
+    s[0, 0, 5000:5100] = s[0, 0, 777]
+    seq = np.array([64 * NBr - 5], dtype=np.int32)
+    for k, ns, nr in ((1, 1, 0), (2000, 1, 64), (NBr // 2, 0, 0), (NBr, 1, 64)):
+        idx, n = skv.attn_select_topk(torch.from_numpy(s).cuda(), torch.from_numpy(seq).cuda(), k=k,
+                                      n_sink_blocks=ns, n_recent_blocks=nr)
+        torch.cuda.synchronize()
+        idx, n = idx.cpu().numpy(), n.cpu().numpy()
+        ref = oracle.select_all(s.astype(np.float64), seq, k, ns, nr)
+        for g in range(Hkv):
+            assert n[0, g] == len(ref[0][g]), (k, g)
+            assert idx[0, g, :n[0, g]].tolist() == ref[0][g], (k, g)
