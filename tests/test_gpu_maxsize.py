@@ -126,3 +126,26 @@ def test_topk_rows_longer_than_the_staged_keys(NBr):
         for g in range(Hkv):
             assert n[0, g] == len(ref[0][g]), (k, g)
             assert idx[0, g, :n[0, g]].tolist() == ref[0][g], (k, g)
+
+
+@pytest.mark.parametrize("path", ["one", "ws"])
+def test_art_on_a_2gib_slice(max_slice, path):
+    # two properties that hold at any size ("ART" summary, §2.2-2.3): tau = phi = 0 never stops, so ART
+    # folds all 131072 blocks and equals dense attention; tau = phi = inf with p = 1 stops at visit
+    # position 1, after block 0 and the newest block
+    import sparse_kv_amd as skv
+
+    q, k, v, desc = max_slice
+    log(f"[max] ART over a 2 GiB slice ({path})")
+    ws = torch.empty(max(skv.attn_art_workspace_bytes(q, k), 1), dtype=torch.uint8, device="cuda")
+    run = (lambda **kw: skv.attn_decode_art_ws(q, k, v, None, workspace=ws, **kw)) if path == "ws" else \
+        (lambda **kw: skv.attn_decode_art(q, k, v, None, **kw))
+    out, stop, fetched = run(tau=0.0, phi=0.0, patience=2, probe_dim=8)
+    torch.cuda.synchronize()
+    assert int(stop[0, 0]) == NB - 1 and int(fetched[0, 0]) == NB
+    assert_close(out.cpu().numpy()[0, 0], exact_output(desc, [(0, N)]), TOL, f"ART tau=phi=0 ({path})")
+    out, stop, fetched = run(tau=math.inf, phi=math.inf, patience=1, probe_dim=8)
+    torch.cuda.synchronize()
+    assert int(stop[0, 0]) == 1
+    assert_close(out.cpu().numpy()[0, 0], exact_output(desc, [(0, 64), (N - 64, N)]), TOL,
+                 f"ART tau=phi=inf p=1 ({path})")
