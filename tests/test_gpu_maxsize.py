@@ -1,6 +1,7 @@
 """GPU parity at the size limits: a (b, kv head) K/V slice of exactly 2 GiB
 (131072 blocks of bf16 d 128, the largest the library accepts) and top-k rows
-longer than the candidates a workgroup stages in LDS.
+longer than the candidates a workgroup stages in LDS; a paged pool whose blocks
+all lie past byte offset 2^32.
 
 The 2 GiB slice is built on the device: zero keys and values except a few
 tokens, so the exact attention output has a closed form (softmax attention
@@ -16,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_util import TOL, assert_close, log
+from tests.gpu_util import TOL, assert_close, log, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -149,3 +150,38 @@ def test_art_on_a_2gib_slice(max_slice, path):
     assert int(stop[0, 0]) == 1
     assert_close(out.cpu().numpy()[0, 0], exact_output(desc, [(0, 64), (N - 64, N)]), TOL,
                  f"ART tau=phi=inf p=1 ({path})")
+
+
+def test_paged_pool_past_4gib():
+    # pool runs placed past byte offset 2^32 of the pool: the per-block offsets need 64 bits
+    import sparse_kv_amd as skv
+    import synth
+
+    log("[max] paged decode with every block stored past 4 GiB into the pool")
+    B, Hq, Hkv, d, NBl = 2, 8, 2, 128, 40
+    inp = synth.make_inputs(77, B, Hq, Hkv, d, 64 * NBl, kind="gauss", seq_lens=[64 * NBl, 64 * 23 + 7])
+    q, k, v, sl = upload(inp)
+    P = 140000  # 140000 x 2 heads x 16 KiB = 4.6 GB per pool
+    first = (1 << 32) // (Hkv * 64 * d * 2) + 11  # first slot whose offset is past 2^32
+    assert first + B * NBl < P
+    perm = torch.randperm(B * NBl, generator=torch.Generator().manual_seed(3)) + first
+    table = perm.view(B, NBl).to(torch.int32).cuda()
+    kp = torch.full((P, Hkv, 64, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vp = torch.full((P, Hkv, 64, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kb = k.view(B, Hkv, NBl, 64, d).permute(0, 2, 1, 3, 4).reshape(B * NBl, Hkv, 64, d)
+    vb = v.view(B, Hkv, NBl, 64, d).permute(0, 2, 1, 3, 4).reshape(B * NBl, Hkv, 64, d)
+    kp[table.view(-1).long()] = kb
+    vp[table.view(-1).long()] = vb
+    qf, kf, vf = inp.f64()
+    ref = oracle.decode_dense(qf, kf, vf, inp.seq_lens, inp.scale)
+    out = skv.attn_merge_states(*skv.attn_decode_dense_paged(q, kp, vp, table, sl, num_splits=3))
+    contiguous = skv.attn_merge_states(*skv.attn_decode_dense(q, k, v, sl, num_splits=3))
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, TOL, "dense over a pool past 4 GiB")
+    assert torch.equal(out, contiguous), "paged and contiguous dense outputs differ"
+    ao, astop, _ = skv.attn_decode_art_paged(q, kp, vp, table, sl, tau=0.0, phi=0.0, patience=2, probe_dim=8)
+    torch.cuda.synchronize()
+    assert (astop.cpu().numpy() == np.array([[NBl - 1] * Hq, [23] * Hq])).all()
+    assert_close(ao.cpu().numpy(), ref, TOL, "ART (tau = phi = 0) over a pool past 4 GiB")
+    del kp, vp
+    torch.cuda.empty_cache()
