@@ -141,7 +141,7 @@ struct LdsRing {
 // for its state stores to complete before it stores the position, the
 // folder issues its state loads only after it has read the position, and it
 // waits for them to complete before it advances the window.
-template <int GP, int D, int R, int NF>
+template <int GP, int D, int R, int NF, int EP = 4>
 struct GlobalRing {
   static constexpr int kR = R;
   static constexpr int kMaxBatch = R / 2;  // the producers work on the other half
@@ -167,8 +167,12 @@ struct GlobalRing {
     ctrl = (int*)(u + kCtrlOff);
     rs = make_rsrc(u, kBytes);
   }
+  // channel col of a row: producer lane l holds channels l EP .. l EP + EP - 1
+  // and stores them as EP / 4 16-byte pieces; piece h of every lane is laid
+  // out contiguously, so each store instruction covers whole 32-byte sectors
   static __device__ uint32_t acc_off(int s, int q, int col) {
-    return kAccOff + (((uint32_t)s * GP + q) * D + col) * 4;
+    const uint32_t l = (uint32_t)col / EP, h = ((uint32_t)col % EP) / 4, w = (uint32_t)col % 4;
+    return kAccOff + ((uint32_t)s * GP + q) * D * 4 + (h * (D / EP) + l) * 16 + w * 4;
   }
   template <int E>
   __device__ void put_acc(int s, int q, int col, const float (&v)[E]) {
@@ -788,7 +792,7 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* 
   using SH = ArtMcShared<T, D, GR, NP>;
   constexpr int NF = 4 * GR;  // one folder wave per query head
   static_assert(NF <= kMaxFolders && NF <= NP + 1, "folder waves");
-  using RING = GlobalRing<4 * GR, D, R, NF>;
+  using RING = GlobalRing<4 * GR, D, R, NF, Geo<T, D>::E>;
   __shared__ SH sh;
   const int units = p.B * p.Hkv;
   const int unit = blockIdx.x % units;
