@@ -157,3 +157,16 @@ def test_art_workspace_reused_across_calls():
         assert np.array_equal(stop, ref_stop), (seed, stop, ref_stop)
         assert_close(out, ref_out, TOL, f"ART output, seed {seed}")
         check_fetched(fetched, stop, inp, "ws")
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("probe", [1, 3, 12, 16])
+def test_art_probe_widths(probe, path):
+    # probes narrower than 8 channels, and wider ones (the scan then carries 16)
+    log(f"[art] probe_dim = {probe} ({path})")
+    inp, ref_out, ref_stop = art_inputs(41, 2, 8, 2, 128, 64 * 40, seq=[64 * 40, 64 * 33 + 9], probe=probe)
+    out, stop, fetched = run_art(inp, probe=probe, path=path)
+    log(f"  stops {ref_stop.ravel().tolist()}")
+    assert np.array_equal(stop, ref_stop), (stop, ref_stop)
+    assert_close(out, ref_out, TOL, f"ART output, probe {probe}")
+    check_fetched(fetched, stop, inp, path)
