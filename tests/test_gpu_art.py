@@ -170,3 +170,16 @@ def test_art_probe_widths(probe, path):
     assert np.array_equal(stop, ref_stop), (stop, ref_stop)
     assert_close(out, ref_out, TOL, f"ART output, probe {probe}")
     check_fetched(fetched, stop, inp, path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("p", [1, 3, 5])
+def test_art_patience(p, path):
+    # the stop needs p consecutive stable steps ("ART" summary, §2.3)
+    log(f"[art] patience {p} ({path})")
+    inp, ref_out, ref_stop = art_inputs(42, 2, 8, 2, 128, 64 * 40, seq=[64 * 40, 64 * 31 + 3], p=p)
+    out, stop, fetched = run_art(inp, p=p, path=path)
+    log(f"  stops {ref_stop.ravel().tolist()}")
+    assert np.array_equal(stop, ref_stop), (stop, ref_stop)
+    assert_close(out, ref_out, TOL, f"ART output, patience {p}")
+    check_fetched(fetched, stop, inp, path)
