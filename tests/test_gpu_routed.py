@@ -11,11 +11,17 @@ from tests.gpu_util import TOL, assert_close, log, upload
 pytestmark = pytest.mark.gpu
 
 
-def test_routed_stack_matches_oracle():
-    log("[routed] 6-layer stack, sink + window layers poisoned outside their blocks")
-    n_layers, B, Hq, Hkv, d, L = 6, 2, 8, 2, 128, 64 * 40
+@pytest.mark.parametrize("mask,n_shards,sps,sa_splits", [
+    ([1, 0, 0, 1, 1, 0], 8, 2, 3),    # mixed stack
+    ([1, 1, 1], 1, 1, 1),              # every layer full, one shard of one split
+    ([0, 0, 0], 3, 5, 7),              # every layer sink + window
+    ([0, 1, 1, 0], 8, 4, 32),          # the benchmark's split counts
+])
+def test_routed_stack_matches_oracle(mask, n_shards, sps, sa_splits):
+    log(f"[routed] {len(mask)}-layer stack {mask}, {n_shards} shards x {sps} splits, {sa_splits} SA splits; "
+        "sink + window layers poisoned outside their blocks")
+    n_layers, B, Hq, Hkv, d, L = len(mask), 2, 8, 2, 128, 64 * 40
     seq = [64 * 40, 64 * 29 + 3]
-    mask = [1, 0, 0, 1, 1, 0]
     n_sink, n_recent = 1, 6
     import sparse_kv_amd as skv
 
@@ -35,7 +41,8 @@ def test_routed_stack_matches_oracle():
     idx, n = skv.attn_select_topk(None, sl, k=0, n_sink_blocks=n_sink, n_recent_blocks=n_recent,
                                   shape=(B, Hkv, L // 64))
     outs = skv.attn_decode_routed([x[0] for x in layers], [x[1] for x in layers], [x[2] for x in layers], mask,
-                                  sl, n_shards=8, splits_per_shard=2, sa_block_idx=idx, sa_n_sel=n, sa_splits=3)
+                                  sl, n_shards=n_shards, splits_per_shard=sps, sa_block_idx=idx, sa_n_sel=n,
+                                  sa_splits=sa_splits)
     torch.cuda.synchronize()
     ref = oracle.routed_layer_outputs(host, np.array(seq), 1 / np.sqrt(d), mask, n_sink, n_recent)
     for i in range(n_layers):
