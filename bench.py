@@ -89,7 +89,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", default="dense,sparse,art,window",
-                    help="comma list of dense, sparse, art, window, art_imp, sparse2, dense_paged")
+                    help="comma list of dense, sparse, art, window (the step), and art_imp, sparse2, dense_paged, "
+                         "art_sel, sparse_fc, centroid_upd")
     ap.add_argument("--splits-per-shard", type=int, default=4, help="hybrid256k: inner splits per context shard")
     ap.add_argument("--sa-splits", type=int, default=32, help="hybrid256k: splits of a sink+window layer")
     ap.add_argument("--workload", default="decode128k", choices=["decode128k", "art64k", "hybrid256k", "dense32k"],
@@ -140,7 +141,8 @@ def main():
     q = up(inp.q)
     copies = {}
     k0, v0 = up(inp.k), up(inp.v)
-    for i, s in enumerate(("dense", "sparse", "art", "window", "art_imp", "sparse2")):
+    for i, s in enumerate(("dense", "sparse", "art", "window", "art_imp", "sparse2", "art_sel", "sparse_fc",
+                           "centroid_upd")):
         if s in stages or s == "dense":
             copies[s] = (k0, v0) if i == 0 else (k0.clone(), v0.clone())
     torch.cuda.synchronize()
@@ -163,6 +165,12 @@ def main():
 
         kpool, vpool = to_pool(k0), to_pool(v0)
         ptable = perm.view(B, NB).to(torch.int32).contiguous()
+    # ART over the top-k selection; selection by a per-KV-head forecast vector; the per-step centroid refresh
+    C_sel = skv.attn_build_centroids(copies["art_sel"][0]) if "art_sel" in stages else None
+    C_fc = skv.attn_build_centroids(copies["sparse_fc"][0]) if "sparse_fc" in stages else None
+    C_up = skv.attn_build_centroids(copies["centroid_upd"][0]) if "centroid_upd" in stages else None
+    fcq = torch.randn((B, Hkv, d), generator=torch.Generator().manual_seed(11)).to(torch.bfloat16).to(dev)
+    prev_lens = torch.full((B,), L - 1, dtype=torch.int32, device=dev)  # one token appended per row
     group2, kc2 = 16, 32
     C_2 = skv.attn_build_centroids(copies["sparse2"][0]) if "sparse2" in stages else None
     C2_2 = skv.attn_build_super_centroids(C_2, group2) if "sparse2" in stages else None
@@ -194,6 +202,15 @@ def main():
     # ART spreads each (b, kv head) over several CUs through this workspace when B * Hkv is small
     art_ws = torch.empty(max(skv.attn_art_workspace_bytes(q, k0), 1), dtype=torch.uint8, device=dev)
     out_i = torch.empty((B, Hq, d), **f32)
+    scores_a, scores_f = torch.empty((B, Hkv, NB), **f32), torch.empty((B, Hkv, NB), **f32)
+    sela_idx = torch.empty((B, Hkv, max_sel), dtype=torch.int32, device=dev)
+    sela_n = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    self_idx = torch.empty((B, Hkv, max_sel), dtype=torch.int32, device=dev)
+    self_n = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    out_as, out_f = torch.empty((B, Hq, d), **f32), torch.empty((B, Hq, d), **f32)
+    stop_as = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    fetched_as = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    st_f = (torch.empty((B, Hq, Ss), **f32), torch.empty((B, Hq, Ss), **f32), torch.empty((B, Hq, Ss, d), **f32))
     stop_i = torch.empty((B, Hq), dtype=torch.int32, device=dev)
     fetched_i = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
 
@@ -265,6 +282,30 @@ def main():
                                    probe_dim=probe, workspace=art_ws, out=out_i, stop_pos=stop_i,
                                    blocks_fetched=fetched_i)
             mark("art_imp.1")
+        if "art_sel" in stages:
+            ka, va = copies["art_sel"]
+            mark("art_sel.0")
+            skv.attn_score_centroids(q, C_sel, None, out=scores_a)
+            skv.attn_select_topk(scores_a, None, k=topk, n_sink_blocks=n_sink, n_recent_blocks=n_recent,
+                                 max_sel=max_sel, block_idx=sela_idx, n_sel=sela_n)
+            mark("art_sel.sel")
+            skv.attn_decode_art_list_ws(q, ka, va, sela_idx, sela_n, None, tau=tau, phi=phi, patience=patience,
+                                        probe_dim=probe, workspace=art_ws, out=out_as, stop_pos=stop_as,
+                                        blocks_fetched=fetched_as)
+            mark("art_sel.1")
+        if "sparse_fc" in stages:
+            kf_, vf_ = copies["sparse_fc"]
+            mark("sparse_fc.0")
+            skv.attn_score_centroids(fcq, C_fc, None, scale=d ** -0.5, out=scores_f)
+            skv.attn_select_topk(scores_f, None, k=topk, n_sink_blocks=n_sink, n_recent_blocks=n_recent,
+                                 max_sel=max_sel, block_idx=self_idx, n_sel=self_n)
+            skv.attn_decode_sparse(q, kf_, vf_, self_idx, self_n, None, num_splits=Ss, m=st_f[0], l=st_f[1], o=st_f[2])
+            skv.attn_merge_states(*st_f, out=out_f)
+            mark("sparse_fc.1")
+        if "centroid_upd" in stages:
+            mark("centroid_upd.0")
+            skv.attn_update_centroids(copies["centroid_upd"][0], C_up, None, prev_lens=prev_lens, span_hint=1)
+            mark("centroid_upd.1")
 
     for _ in range(args.warmup):
         step(None)
@@ -366,8 +407,33 @@ def main():
             paths["art_imp"]["max_abs_err_vs_dense"] = float((out_i.double() - ref).abs().max())
             if "art" in stages:
                 paths["art"]["max_abs_err_vs_dense"] = float((out_a.double() - ref).abs().max())
+    if "art_sel" in stages:
+        stp = stop_as.cpu().numpy().reshape(B, Hkv, Hq // Hkv)
+        need = stp.max(axis=2) + 1
+        ms = avg_ms("art_sel.0", "art_sel.1")
+        by = (float(need.sum()) * kv_block + units * NB * d * 4 + units * NB * 4 * 2 + float(need.sum()) * 4
+              + q_bytes + o_bytes)
+        total_bytes += by
+        paths["art_sel"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), select_ms=avg_ms("art_sel.0", "art_sel.sel"),
+                                art_ms=avg_ms("art_sel.sel", "art_sel.1"), mean_stop=float(stp.mean()),
+                                listed_per_unit=float(sela_n.cpu().numpy().mean()),
+                                blocks_needed_per_unit=float(need.mean()),
+                                blocks_fetched_per_unit=float(fetched_as.cpu().numpy().mean()),
+                                tokens_per_s=B / (ms * 1e-3))
+    if "sparse_fc" in stages:
+        nf = self_n.cpu().numpy()
+        ms = avg_ms("sparse_fc.0", "sparse_fc.1")
+        by = float(nf.sum()) * kv_block + units * NB * d * 4 + units * NB * 4 * 2 + q_bytes + o_bytes
+        total_bytes += by
+        paths["sparse_fc"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), blocks_per_unit=float(nf.mean()),
+                                  tokens_per_s=B / (ms * 1e-3), splits=Ss)
+    if "centroid_upd" in stages:
+        ms = avg_ms("centroid_upd.0", "centroid_upd.1")
+        by = units * (kv_block // 2) + units * d * 4  # the last block's K read, its centroid written
+        total_bytes += by
+        paths["centroid_upd"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), blocks_per_unit=1)
     if "dense" in paths:
-        for k_ in ("sparse", "art", "window", "art_imp", "sparse2", "dense_paged"):
+        for k_ in ("sparse", "art", "window", "art_imp", "sparse2", "dense_paged", "art_sel", "sparse_fc"):
             if k_ in paths:
                 paths[k_]["speedup_vs_dense"] = paths["dense"]["ms"] / paths[k_]["ms"]
 
