@@ -104,7 +104,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the decode path is single-device; see DESIGN.md for how it would shard).", file=sys.stderr)
+              "(the decode path is single-device; across GPUs it would shard by (batch row, KV head) units, or by "
+              "sequence ranges whose states attn_merge_states combines).", file=sys.stderr)
         sys.exit(2)
 
     if args.workload == "art64k":

@@ -12,7 +12,7 @@ layer, b, kvh, attempt]))``; every (batch row, KV head) unit is drawn on its
 own, so any unit can be regenerated (``attempt`` > 0 redraws one unit) and
 large inputs are produced in parallel threads.
 
-Value recipes (readings of the workload descriptions; see DESIGN.md):
+Value recipes (readings of the workload descriptions):
 
 * ``gauss``: Q, K, V ~ N(0, 1).
 * ``needles``: as ``gauss`` plus, per unit, ``n_needles`` key positions drawn
