@@ -109,14 +109,14 @@ __global__ __launch_bounds__(256) void centroid_update_kernel(const void* __rest
     centroid_block<T, D>(k, C, b, g, Hkv, j, L, NBmax, threadIdx.x & 63, pg);
 }
 
-// ---- scores: 4 waves x 32 centroid rows per workgroup -------------------
+// ---- scores: 4 waves x 16 centroid rows per workgroup -------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void score_kernel(const void* __restrict__ q, const float* __restrict__ C,
                                                     const int32_t* __restrict__ seq_lens, float* __restrict__ scores,
                                                     int32_t Hq, int32_t Hkv, int32_t NBmax, float scale) {
   constexpr int LPR = D / 4;     // lanes per centroid row, 4 floats each
   constexpr int RPI = 64 / LPR;  // rows per wave-wide load
-  constexpr int ROWS = 32;       // rows per wave
+  constexpr int ROWS = 16;       // rows per wave
   constexpr int IT = ROWS / RPI;
   const int g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int G = Hq / Hkv;
@@ -665,7 +665,7 @@ hipError_t launch_score(const void* q, const float* c, const int32_t* seq_lens, 
                         int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t NBmax,
                         int32_t dtype, float scale, hipStream_t st) {
   if (B == 0) return hipSuccess;
-  const dim3 grid((NBmax + 127) / 128, Hkv, B);
+  const dim3 grid((NBmax + 63) / 64, Hkv, B);
   if (dtype == 1) {
     if (d == 128)
       score_kernel<__bf16, 128><<<grid, 256, 0, st>>>(q, c, seq_lens, scores, Hq, Hkv, NBmax, scale);
