@@ -183,3 +183,21 @@ def test_art_patience(p, path):
     assert np.array_equal(stop, ref_stop), (stop, ref_stop)
     assert_close(out, ref_out, TOL, f"ART output, patience {p}")
     check_fetched(fetched, stop, inp, path)
+
+
+@pytest.mark.parametrize("B", [12, 16])
+def test_art_across_workgroups_at_many_units(B):
+    # 96 and 128 (b, kv head) units: two workgroups per unit on a 256-CU device (four at the smaller
+    # sizes above), and 128 is the largest count the workspace form spreads
+    log(f"[art] {B * 8} units through attn_decode_art_ws")
+    inp, ref_out, ref_stop = art_inputs(43, B, 32, 8, 128, 64 * 20, recent=64 * 6)
+    import sparse_kv_amd as skv
+
+    need = skv.attn_art_workspace_bytes(torch.empty(B, 32, 128, dtype=torch.bfloat16),
+                                        torch.empty(B, 8, 64 * 20, 128, dtype=torch.bfloat16))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 1, "the workspace form should be available at this unit count"
+    out, stop, fetched = run_art(inp, path="ws", workspace=ws)
+    assert np.array_equal(stop, ref_stop), (stop, ref_stop)
+    assert_close(out, ref_out, TOL, f"ART output, {B * 8} units")
+    check_fetched(fetched, stop, inp, "ws")
