@@ -84,8 +84,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--splits", type=int, default=4,
                     help="splits per (batch row, KV head), dense stage (4: one workgroup per CU at batch 8)")
-    ap.add_argument("--sparse-splits", type=int, default=4, help="splits per unit, sparse stage")
-    ap.add_argument("--window-splits", type=int, default=4, help="splits per unit, sink+window stage")
+    ap.add_argument("--sparse-splits", type=int, default=3, help="splits per unit, sparse stage")
+    ap.add_argument("--window-splits", type=int, default=3, help="splits per unit, sink+window stage")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", default="dense,sparse,art,window",
@@ -219,13 +219,16 @@ def main():
     ev = {}
 
     ev_timed = {}
+    # events are created before the passes that record them, so that recording
+    # adds no host work that could let the device run dry between stages
+    ev_pool = [torch.cuda.Event(enable_timing=True) for _ in range(32 * args.steps)]
 
     def step(record):
         # record: "all" (every stage boundary, into ev), "dense" (the dense
         # kernel's two boundaries only, into ev_timed) or None
         def mark(tag):
             if record == "all" or (record == "dense" and tag.startswith("dense_kernel")):
-                e = torch.cuda.Event(enable_timing=True)
+                e = ev_pool.pop() if ev_pool else torch.cuda.Event(enable_timing=True)
                 e.record()
                 (ev if record == "all" else ev_timed).setdefault(tag, []).append(e)
 
