@@ -33,7 +33,8 @@
 // unit over up to 4 workgroups (art_mc_kernel below): the ring moves to a
 // caller-provided workspace in device memory (128 slots, device-scope
 // accesses), producers claim visit positions from a per-unit counter, and
-// one folder wave per query head folds batches of up to 64 positions.
+// four folder waves (one per query head, or per two heads when G > 4) fold
+// batches of up to 64 (32) positions.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -775,7 +776,7 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
 // workgroup to finish reports the fetch count.
 template <int GP, int D, int R>
 __global__ __launch_bounds__(128) void art_ring_init(char* ws) {
-  using RING = GlobalRing<GP, D, R, GP>;
+  using RING = GlobalRing<GP, D, R, 4>;
   RING ring(ws, blockIdx.x);
   if (threadIdx.x < R) ring.pos[threadIdx.x] = -1;
   if (threadIdx.x < RING::kNumCtrl) ring.ctrl[threadIdx.x] = 0;
@@ -790,8 +791,11 @@ struct ArtMcShared : ArtWaves<T, D, GR, NP> {
 template <typename T, int D, int GR, int NP, int R>
 __global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* ws, int groups) {
   using SH = ArtMcShared<T, D, GR, NP>;
-  constexpr int NF = 4 * GR;  // one folder wave per query head
-  static_assert(NF <= kMaxFolders && NF <= NP + 1, "folder waves");
+  // folder waves: one per query head for G <= 4, one per two heads for G <= 8,
+  // so the folding workgroup always keeps NP + 1 - NF producer waves of its
+  // own (its unit progresses even if no other workgroup of it is resident)
+  constexpr int NF = 4;
+  static_assert(NF <= kMaxFolders && NF < NP, "folder waves and producers of the folding workgroup");
   using RING = GlobalRing<4 * GR, D, R, NF, Geo<T, D>::E>;
   __shared__ SH sh;
   const int units = p.B * p.Hkv;
@@ -813,7 +817,7 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* 
   const bool folds = sh.role == 0;
   if (folds && w < NF) {
     __builtin_amdgcn_s_setprio(3);
-    art_fold<T, D, 1>(p, sh, ring, __builtin_amdgcn_readfirstlane(w), b, g, G, nv);
+    art_fold<T, D, GR>(p, sh, ring, __builtin_amdgcn_readfirstlane(w), b, g, G, nv);
   } else if (w > 0) {
     ClaimedPositions pos{&ring.ctrl[RING::kNext]};
     art_producer<T, D, GR>(p, sh, ring, pos, __builtin_amdgcn_readfirstlane(w - 1), unit, b, g, G, L, nb, nv);
@@ -832,7 +836,7 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* 
 
 template <int D>
 constexpr size_t art_ring_bytes(int G) {
-  return G > 4 ? GlobalRing<8, D, kArtRingSlots, 8>::kBytes : GlobalRing<4, D, kArtRingSlots, 4>::kBytes;
+  return G > 4 ? GlobalRing<8, D, kArtRingSlots, 4>::kBytes : GlobalRing<4, D, kArtRingSlots, 4>::kBytes;
 }
 
 template <typename T, int D, int GR>
@@ -852,9 +856,10 @@ template <typename T, int D>
 hipError_t launch_art_t(const ArtArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int units = a.B * a.Hkv;
+  // the form depends on the CU count of the device the work is queued on
   int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+  const hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   if (ws && units <= kArtMcMaxUnits && 2 * units <= cus && ws_bytes >= (size_t)units * art_ring_bytes<D>(G)) {
     const int groups = min(kArtMcMaxGroups, cus / units);

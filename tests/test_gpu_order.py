@@ -9,6 +9,7 @@ import torch
 import oracle
 import synth
 from oracle.art import art_margin_ok
+from oracle.selection import selection_gap
 from tests.gpu_util import TOL, assert_close, log, upload
 
 pytestmark = pytest.mark.gpu
@@ -130,46 +131,105 @@ def art_list(path):
     return skv.attn_decode_art_list_ws if path == "ws" else skv.attn_decode_art_list
 
 
+def list_case(cfg, B, Hq, Hkv, d, L, seq, kind, k, ns, nr, max_list, newest_first=False, require_inside=False,
+              recent=64 * 5):
+    """Inputs and block lists for ART over a selection: per unit the oracle's top-k list
+    (ascending, so block 0 first), or block 0 then the other listed blocks newest first.
+    Units are redrawn until every top-k boundary gap exceeds 1e-4, every thresholded ART
+    decision clears the 1% band and, with require_inside, every head stops strictly
+    inside its list.  Returns (inputs, lists, block_list, n_list)."""
+    attempts = {}
+    G = Hq // Hkv
+    for _ in range(40):
+        inp = synth.make_inputs(cfg, B, Hq, Hkv, d, L, kind=kind, seq_lens=seq, attempts=attempts,
+                                recent_tokens=recent)
+        qf, kf, vf = inp.f64()
+        sc = oracle.centroid_scores(qf, oracle.block_centroids(kf, inp.seq_lens), inp.seq_lens, inp.scale)
+        lists = oracle.select_all(sc, inp.seq_lens, k, ns, nr)
+        bl = np.full((B, Hkv, max_list), -1, dtype=np.int32)
+        nl = np.zeros((B, Hkv), dtype=np.int32)
+        bad = set()
+        for b in range(B):
+            nb = -(-int(inp.seq_lens[b]) // 64)
+            for g in range(Hkv):
+                x = lists[b][g]
+                if newest_first:
+                    x = x[:1] + sorted(x[1:], reverse=True)
+                bl[b, g, :len(x)] = x
+                nl[b, g] = len(x)
+                if not selection_gap(sc[b, g], nb, k, ns, nr) > 1e-4:
+                    bad.add((b, g))
+        _, stop, traces = oracle.art_decode(qf, kf, vf, inp.seq_lens, inp.scale, TAU, PHI, P, PROBE, order=bl,
+                                            n_visit=nl)
+        bad |= {(b, h // G) for (b, h), tr in traces.items() if not art_margin_ok(tr, TAU, PHI)}
+        if require_inside:
+            bad |= {(b, h // G) for b in range(B) for h in range(Hq) if not stop[b, h] < nl[b, h // G] - 1}
+        if not bad:
+            return inp, lists, bl, nl
+        for u in bad:
+            attempts[u] = attempts.get(u, 0) + 1
+    raise AssertionError("could not draw list inputs with selection and ART decision margins")
+
+
+def run_art_list(path, inp, lists, bl, nl, tau, phi, p):
+    """ART over the lists on a copy of the cache whose unlisted blocks hold NaN."""
+    poisoned = synth.DecodeInputs(inp.q, inp.k.copy(), inp.v.copy(), inp.seq_lens, inp.dtype)
+    synth.poison_blocks(poisoned, lists)
+    q, k, v, sl = upload(poisoned)
+    out, stop, fetched = art_list(path)(q, k, v, dev_i32(bl), dev_i32(nl), sl, tau=tau, phi=phi, patience=p,
+                                        probe_dim=PROBE)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), stop.cpu().numpy(), fetched.cpu().numpy()
+
+
 @pytest.mark.parametrize("path", ["one", "ws"])
 def test_art_over_selected_lists(path):
     """attn_decode_art_list[_ws] on the oracle's top-k lists; unlisted blocks hold NaN."""
     log(f"[order] ART over top-k lists (sink first, ascending), {path}")
     B, Hq, Hkv, d, L = 2, 8, 2, 128, 64 * 48
-    seq = [64 * 48, 64 * 31 + 20]
-    inp = synth.make_inputs(61, B, Hq, Hkv, d, L, kind="recency", seq_lens=seq, recent_tokens=64 * 5)
+    inp, lists, bl, nl = list_case(61, B, Hq, Hkv, d, L, [64 * 48, 64 * 31 + 20], "recency", 12, 1, 4, 20)
     qf, kf, vf = inp.f64()
-    sc = oracle.centroid_scores(qf, oracle.block_centroids(kf, inp.seq_lens), inp.seq_lens, inp.scale)
-    lists = oracle.select_all(sc, inp.seq_lens, 12, 1, 4)
-    max_list = 20
-    bl = np.full((B, Hkv, max_list), -1, dtype=np.int32)
-    nl = np.zeros((B, Hkv), dtype=np.int32)
-    for b in range(B):
-        for g in range(Hkv):
-            bl[b, g, :len(lists[b][g])] = lists[b][g]
-            nl[b, g] = len(lists[b][g])
     for tau, phi, p in ((TAU, PHI, P), (0.0, 0.0, 1), (math.inf, math.inf, 1)):
-        ref_out, ref_stop, traces = oracle.art_decode(qf, kf, vf, inp.seq_lens, inp.scale, tau, phi, p, PROBE,
-                                                      order=bl, n_visit=nl)
-        if not all(art_margin_ok(tr, tau, phi) for tr in traces.values()):
-            assert tau == TAU
-            log("  (thresholded case lacks margins at this seed; skipped)")
-            continue
-        poisoned = synth.DecodeInputs(inp.q, inp.k.copy(), inp.v.copy(), inp.seq_lens, inp.dtype)
-        synth.poison_blocks(poisoned, lists)
-        q, k, v, sl = upload(poisoned)
-        out, stop, fetched = art_list(path)(q, k, v, dev_i32(bl), dev_i32(nl), sl, tau=tau, phi=phi,
-                                            patience=p, probe_dim=PROBE)
-        torch.cuda.synchronize()
-        stop, fetched = stop.cpu().numpy(), fetched.cpu().numpy()
+        ref_out, ref_stop, _ = oracle.art_decode(qf, kf, vf, inp.seq_lens, inp.scale, tau, phi, p, PROBE,
+                                                 order=bl, n_visit=nl)
+        out, stop, fetched = run_art_list(path, inp, lists, bl, nl, tau, phi, p)
         log(f"  tau={tau}: stops {stop.ravel().tolist()}")
         assert np.array_equal(stop, ref_stop)
-        assert_close(out.cpu().numpy(), ref_out, TOL, f"ART over lists tau={tau}")
+        assert_close(out, ref_out, TOL, f"ART over lists tau={tau}")
         assert (fetched <= nl).all()
         if tau == 0.0:
             assert (stop == nl.repeat(Hq // Hkv, axis=1) - 1).all()
             dense_lists = oracle.decode_blocks(qf, kf, vf, inp.seq_lens, inp.scale,
                                                [[sorted(x) for x in row] for row in lists])
-            assert_close(out.cpu().numpy(), dense_lists, TOL, "tau = 0 equals attention over the lists")
+            assert_close(out, dense_lists, TOL, "tau = 0 equals attention over the lists")
+        if tau == math.inf:
+            assert (stop == 1).all()
+
+
+@pytest.mark.parametrize("path", ["one", "ws"])
+@pytest.mark.parametrize("label,cfg,L,seq,kind,k,nr,newest_first", [
+    ("recency keys, newest listed block first, 17 listed", 63, 64 * 48, [64 * 48, 64 * 37 + 20], "recency", 12, 4,
+     True),
+    ("mixture keys, ascending lists, 89 listed", 64, 64 * 400, [64 * 400, 64 * 350 - 7], "mixture", 80, 8, False),
+])
+def test_art_over_lists_stops_inside_the_list(label, cfg, L, seq, kind, k, nr, newest_first, path):
+    """Finite thresholds (tau 1e-3, phi 1e-4, p 2) stop every head strictly inside its list
+    ("ART" summary §2.4: the stop rule as a control layer over a selection); stops exact,
+    outputs within tolerance, unlisted blocks NaN, read-ahead within the list."""
+    log(f"[order] ART over lists, stop inside: {label}, {path}")
+    B, Hq, Hkv, d = 2, 8, 2, 128
+    inp, lists, bl, nl = list_case(cfg, B, Hq, Hkv, d, L, seq, kind, k, 1, nr, k + 1 + nr + 3,
+                                   newest_first=newest_first, require_inside=True)
+    qf, kf, vf = inp.f64()
+    ref_out, ref_stop, _ = oracle.art_decode(qf, kf, vf, inp.seq_lens, inp.scale, TAU, PHI, P, PROBE, order=bl,
+                                             n_visit=nl)
+    assert (ref_stop < nl.repeat(Hq // Hkv, axis=1) - 1).all()
+    out, stop, fetched = run_art_list(path, inp, lists, bl, nl, TAU, PHI, P)
+    log(f"  lists of {nl.ravel().tolist()}: stops {stop.ravel().tolist()}, fetched {fetched.ravel().tolist()}")
+    assert np.array_equal(stop, ref_stop)
+    assert_close(out, ref_out, TOL, "ART over lists, stopped inside")
+    need = stop.reshape(B, Hkv, -1).max(axis=2) + 1
+    assert (need <= fetched).all() and (fetched <= nl).all()
 
 
 @pytest.mark.parametrize("path", ["one", "ws"])
