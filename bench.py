@@ -132,7 +132,7 @@ def main():
     torch.cuda.set_device(dev)
 
     t0 = time.perf_counter()
-    inp = synth.make_inputs(3, B, Hq, Hkv, d, L, dtype="bf16", kind="mixture")
+    inp = synth.workload_inputs(3)  # units whose decisions would sit inside the margins are redrawn
     gen_s = time.perf_counter() - t0
     print(f"[bench] generated 128K batch-8 inputs in {gen_s:.1f}s", file=sys.stderr, flush=True)
 
@@ -558,7 +558,7 @@ def bench_art64k(args):
     W = synth.WORKLOADS[4]
     B, Hq, Hkv, d, L = W["B"], W["Hq"], W["Hkv"], W["d"], W["L"]
     dev = torch.device("cuda", 0)
-    inp = synth.make_inputs(4, B, Hq, Hkv, d, L, kind="recency")
+    inp = synth.workload_inputs(4)
     up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
     q, k, v = up(inp.q), up(inp.k), up(inp.v)
     del inp
