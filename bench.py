@@ -88,6 +88,9 @@ def parse():
     ap.add_argument("--window-splits", type=int, default=3, help="splits per unit, sink+window stage")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (32K batch 8 dense, 64K batch 32 ART, the 36-layer 256K stack) "
+                         "and the read-ceiling probe that the default run adds to the line")
     ap.add_argument("--stages", default="dense,sparse,art,window",
                     help="comma list of dense, sparse, art, window (the step), and art_imp, sparse2, dense_paged, "
                          "art_sel, sparse_fc, centroid_upd")
@@ -327,6 +330,18 @@ def main():
     for _ in range(args.steps):
         step("all")
     torch.cuda.synchronize()
+    # detector overhead of both ART launch forms on this input: tau = phi = 0 (no stop, every probe
+    # compared) against the detector off; every block of every unit is folded either way
+    art_overhead = {}
+    if "art" in stages:
+        ka, va = copies["art"]
+        o_, s_, f_ = torch.empty_like(out_a), torch.empty_like(stop), torch.empty_like(fetched)
+        art_overhead["across_workgroups"] = detector_overhead(
+            lambda **kw: skv.attn_decode_art_ws(q, ka, va, None, workspace=art_ws, out=o_, stop_pos=s_,
+                                                blocks_fetched=f_, **kw), patience)
+        art_overhead["one_workgroup"] = detector_overhead(
+            lambda **kw: skv.attn_decode_art(q, ka, va, None, out=o_, stop_pos=s_, blocks_fetched=f_, **kw),
+            patience, reps=3)
 
     def avg_ms(a, b, evs=None):
         evs = ev if evs is None else evs
@@ -357,15 +372,13 @@ def main():
         paths["sparse"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), blocks_per_unit=float(n_sel.mean()),
                                tokens_per_s=B / (ms * 1e-3), splits=Ss)
     if "art" in stages:
-        stp = stop.cpu().numpy().reshape(B, Hkv, Hq // Hkv)
-        need = stp.max(axis=2) + 1
+        st = unit_stats(stop.cpu().numpy(), fetched.cpu().numpy(), Hkv)
         ms = avg_ms("art.0", "art.1")
-        by = float(need.sum()) * kv_block + q_bytes + o_bytes
+        by = st["blocks_needed_per_unit"] * units * kv_block + q_bytes + o_bytes
         total_bytes += by
-        paths["art"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), mean_stop=float(stp.mean()),
-                            blocks_needed_per_unit=float(need.mean()),
-                            blocks_fetched_per_unit=float(fetched.cpu().numpy().mean()),
-                            tokens_per_s=B / (ms * 1e-3), workgroups_per_unit=art_groups(B * Hkv))
+        paths["art"] = dict(ms=ms, bytes=by, gbs=gbs(by, ms), tokens_per_s=B / (ms * 1e-3),
+                            workgroups_per_unit=art_groups(B * Hkv), **st,
+                            detector_overhead_pct=art_overhead)
     if "window" in stages:
         ms = avg_ms("window.0", "window.1")
         by = float(win_n.cpu().numpy().sum()) * kv_block + q_bytes + o_bytes
@@ -462,8 +475,7 @@ def main():
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(paths["dense"]["tokens_per_s"], 1) if "dense" in paths else None,
         "centroid_build_ms": round(centroid_ms, 4),
-        "paths": {k_: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v_.items()}
-                  for k_, v_ in paths.items()},
+        "paths": {k_: rounded(v_) for k_, v_ in paths.items()},
     }
     if "dense" in paths:
         kb = units * NB * kv_block + q_bytes + B * Hq * S * (d + 2) * 4
@@ -472,10 +484,33 @@ def main():
                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                            "traffic": measured_dense_traffic(S), "bytes_per_launch": kb,
                            "avg_launch_ms": round(paths["dense"]["kernel_ms"], 5)}
+    if not args.no_extra:
+        # the other workloads, each on its own inputs; the line's metric stays the 128K step
+        del copies
+        torch.cuda.empty_cache()
+        ceil = run_ceiling()
+        res["ceiling"] = rounded(ceil)
+        if "roofline" in res:
+            res["roofline"]["ceiling_gbs"] = round(ceil["gbs"], 1)
+            res["roofline"]["frac_of_ceiling"] = round(res["roofline"]["achieved"] / ceil["gbs"], 4)
+        if "dense" in res["paths"]:
+            res["paths"]["dense"]["pct_of_ceiling"] = round(100 * paths["dense"]["gbs"] / ceil["gbs"], 2)
+        for name, fn in (("dense32k_b8", run_dense32k), ("art64k_b32", run_art64k),
+                         ("routed256k_36layers", run_hybrid256k)):
+            t = time.perf_counter()
+            r = fn(args)
+            r["pct_of_ceiling"] = 100 * r["gbs"] / ceil["gbs"]
+            res["paths"][name] = rounded(r)
+            print(f"[bench] {name}: {r['ms']:.4f} ms ({time.perf_counter() - t:.1f}s)", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, topk, n_sink, n_recent, win_recent,
                                            tau, phi, patience, probe, total_bytes / units)
     print(json.dumps(res), flush=True)
+
+
+def rounded(d):
+    return {k_: (round(v_, 4) if isinstance(v_, float) else (rounded(v_) if isinstance(v_, dict) else v_))
+            for k_, v_ in d.items()}
 
 
 def _timer():
@@ -499,6 +534,11 @@ def _timer():
             torch.cuda.synchronize()
             return sum(a.elapsed_time(b) for a, b in self.ev) / len(self.ev)
 
+        def median_ms(self):
+            torch.cuda.synchronize()
+            xs = sorted(a.elapsed_time(b) for a, b in self.ev)
+            return xs[len(xs) // 2]
+
     return T()
 
 
@@ -510,7 +550,7 @@ def _line(args, metric, value, unit, ms, config, **extra):
     print(json.dumps(res), flush=True)
 
 
-def bench_dense32k(args):
+def run_dense32k(args):
     """Dense split-KV decode + merge at 32K context, batch 8 (Llama-3.1-8B layer shape, needle keys)."""
     import numpy as np
     import torch
@@ -540,15 +580,41 @@ def bench_dense32k(args):
     by = kv_bytes + B * Hq * d * 2 + B * Hq * d * 4
     kb = kv_bytes + B * Hq * d * 2 + B * Hq * S * (d + 2) * 4
     ms, kms = ts.avg_ms(), tk.avg_ms()
-    _line(args, "dense decode attention HBM GB/s, 32K ctx, batch 8", by / (ms * 1e-3) / 1e9, "GB/s", ms,
-          {"workload": "dense split-KV decode + merge, 32K context, batch 8, 32 q / 8 kv heads, d 128, bf16 KV, "
-                       "needle keys", "batch": B, "context": L, "splits": S, "parallelism": "single-gpu"},
-          tokens_per_s=round(B / (ms * 1e-3), 1), kernel_ms=round(kms, 5),
-          kernel_gbs=round(kb / (kms * 1e-3) / 1e9, 1), pct_of_peak_hbm=round(100 * by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2))
+    del q, k, v
+    torch.cuda.empty_cache()
+    return dict(workload="dense split-KV decode + merge, 32K context, batch 8, 32 q / 8 kv heads, d 128, bf16 KV, "
+                         "needle keys", batch=B, context=L, splits=S, ms=ms, bytes=by, gbs=by / (ms * 1e-3) / 1e9,
+                pct_peak=100 * by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, tokens_per_s=B / (ms * 1e-3), kernel_ms=kms,
+                kernel_gbs=kb / (kms * 1e-3) / 1e9)
 
 
-def bench_art64k(args):
-    """ART on the 64K-context batch-32 recency workload, dense on the same inputs."""
+def bench_dense32k(args):
+    r = run_dense32k(args)
+    _line(args, "dense decode attention HBM GB/s, 32K ctx, batch 8", r["gbs"], "GB/s", r["ms"],
+          {"workload": r["workload"], "batch": r["batch"], "context": r["context"], "splits": r["splits"],
+           "parallelism": "single-gpu"},
+          tokens_per_s=round(r["tokens_per_s"], 1), kernel_ms=round(r["kernel_ms"], 5),
+          kernel_gbs=round(r["kernel_gbs"], 1), pct_of_peak_hbm=round(r["pct_peak"], 2))
+
+
+def unit_stats(stop, fetched, Hkv):
+    """Per (batch row, KV head) unit: blocks needed (the last head's stop + 1) and fetched."""
+    import numpy as np
+
+    B, Hq = stop.shape
+    need = stop.reshape(B, Hkv, Hq // Hkv).max(axis=2) + 1
+    fetched = np.asarray(fetched)
+    return dict(mean_stop=float(stop.mean()), blocks_needed_per_unit=float(need.mean()),
+                blocks_fetched_per_unit=float(fetched.mean()),
+                needed_per_unit_min_median_p90_max=[int(need.min()), float(np.median(need)),
+                                                     float(np.percentile(need, 90)), int(need.max())],
+                slowest_unit_needed=int(need.max()), slowest_unit_fetched=int(fetched.flat[int(np.argmax(need))]),
+                fetched_over_needed=float(fetched.sum() / need.sum()))
+
+
+def run_art64k(args):
+    """ART on the 64K-context batch-32 recency workload (one workgroup per (b, kv head): 256 units), dense
+    on the same cache, and the detector overhead of that form (tau = phi = 0 against the detector off)."""
     import numpy as np
     import torch
 
@@ -562,49 +628,59 @@ def bench_art64k(args):
     up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
     q, k, v = up(inp.q), up(inp.k), up(inp.v)
     del inp
-    out, stop, fetched = skv.attn_decode_art(q, k, v, None, tau=W["tau"], phi=W["phi"], patience=W["patience"],
-                                             probe_dim=W["probe_dim"])
+    art = dict(tau=W["tau"], phi=W["phi"], patience=W["patience"], probe_dim=W["probe_dim"])
+    out, stop, fetched = skv.attn_decode_art(q, k, v, None, **art)
     S = max(1, 256 // (B * Hkv))  # one workgroup per CU
     m, l, o = skv.attn_decode_dense(q, k, v, None, num_splits=S)
     od = skv.attn_merge_states(m, l, o)
-    ta, td, t0, toff = _timer(), _timer(), _timer(), _timer()
+    ta, td = _timer(), _timer()
     for i in range(args.warmup + args.steps):
         rec = i >= args.warmup
         with (ta if rec else _timer()):
-            skv.attn_decode_art(q, k, v, None, tau=W["tau"], phi=W["phi"], patience=W["patience"],
-                                probe_dim=W["probe_dim"], out=out, stop_pos=stop, blocks_fetched=fetched)
+            skv.attn_decode_art(q, k, v, None, out=out, stop_pos=stop, blocks_fetched=fetched, **art)
         with (td if rec else _timer()):
             skv.attn_decode_dense(q, k, v, None, num_splits=S, m=m, l=l, o=o)
             skv.attn_merge_states(m, l, o, out=od)
-    for i in range(3):  # detector overhead: no early exit (tau = phi = 0) vs detector off
-        with t0:
-            skv.attn_decode_art(q, k, v, None, tau=0.0, phi=0.0, patience=W["patience"], probe_dim=W["probe_dim"],
-                                out=out, stop_pos=stop, blocks_fetched=fetched)
-        with toff:
-            skv.attn_decode_art(q, k, v, None, tau=0.0, phi=0.0, patience=W["patience"], probe_dim=0,
-                                out=out, stop_pos=stop, blocks_fetched=fetched)
-    skv.attn_decode_art(q, k, v, None, tau=W["tau"], phi=W["phi"], patience=W["patience"], probe_dim=W["probe_dim"],
-                        out=out, stop_pos=stop, blocks_fetched=fetched)
+    over = detector_overhead(lambda **kw: skv.attn_decode_art(q, k, v, None, out=out, stop_pos=stop,
+                                                              blocks_fetched=fetched, **kw), W["patience"])
+    skv.attn_decode_art(q, k, v, None, out=out, stop_pos=stop, blocks_fetched=fetched, **art)
     ms_a, ms_d = ta.avg_ms(), td.avg_ms()
-    stp = stop.cpu().numpy().reshape(B, Hkv, Hq // Hkv)
-    need = stp.max(axis=2) + 1
+    st = unit_stats(stop.cpu().numpy(), fetched.cpu().numpy(), Hkv)
     kv_block = 64 * d * 4
-    by = float(need.sum()) * kv_block + B * Hq * d * 6
+    by = st["blocks_needed_per_unit"] * B * Hkv * kv_block + B * Hq * d * 6
     by_d = B * Hkv * (L // 64) * kv_block + B * Hq * d * 6
-    _line(args, "ART decode attention effective HBM GB/s (needed blocks / time), 64K ctx, batch 32",
-          by / (ms_a * 1e-3) / 1e9, "GB/s", ms_a,
-          {"workload": "ART decode step, 64K context, batch 32, 32 q / 8 kv heads, d 128, bf16 KV, recency-"
-                       "concentrated keys; tau 1e-3, phi 1e-4, patience 2, probe 8",
-           "batch": B, "context": L, "parallelism": "single-gpu"},
-          tokens_per_s=round(B / (ms_a * 1e-3), 1), dense_ms=round(ms_d, 4),
-          dense_gbs=round(by_d / (ms_d * 1e-3) / 1e9, 1), speedup_vs_dense=round(ms_d / ms_a, 3),
-          mean_stop=round(float(stp.mean()), 3), blocks_needed_per_unit=round(float(need.mean()), 3),
-          blocks_fetched_per_unit=round(float(fetched.float().mean()), 3),
-          detector_overhead_pct=round(100 * (t0.avg_ms() / toff.avg_ms() - 1), 3))
+    del q, k, v
+    torch.cuda.empty_cache()
+    return dict(workload="ART decode step, 64K context, batch 32, 32 q / 8 kv heads, d 128, bf16 KV, recency-"
+                         "concentrated keys; tau 1e-3, phi 1e-4, patience 2, probe 8; one workgroup per unit",
+                batch=B, context=L, ms=ms_a, bytes=by, gbs=by / (ms_a * 1e-3) / 1e9, tokens_per_s=B / (ms_a * 1e-3),
+                dense_ms=ms_d, dense_gbs=by_d / (ms_d * 1e-3) / 1e9, speedup_vs_dense=ms_d / ms_a,
+                detector_overhead_pct=over, **st)
 
 
-def bench_hybrid256k(args):
-    """One decode step of the 36-layer routed stack at 256K context, batch 1."""
+def detector_overhead(call, patience, reps=5):
+    """Percent kernel time of the stop rule when it never fires: tau = phi = 0 (every block folded,
+    every probe compared) against probe_dim = 0 (detector off); the median of interleaved runs."""
+    t_on, t_off = _timer(), _timer()
+    for _ in range(reps):
+        with t_on:
+            call(tau=0.0, phi=0.0, patience=patience, probe_dim=8)
+        with t_off:
+            call(tau=0.0, phi=0.0, patience=patience, probe_dim=0)
+    return 100.0 * (t_on.median_ms() / t_off.median_ms() - 1.0)
+
+
+def bench_art64k(args):
+    r = run_art64k(args)
+    extra = {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items()
+             if k_ not in ("workload", "batch", "context", "ms", "gbs")}
+    _line(args, "ART decode attention effective HBM GB/s (needed blocks / time), 64K ctx, batch 32", r["gbs"],
+          "GB/s", r["ms"], {"workload": r["workload"], "batch": r["batch"], "context": r["context"],
+                            "parallelism": "single-gpu"}, **extra)
+
+
+def run_hybrid256k(args):
+    """One decode step of the 36-layer routed stack at 256K context, batch 1, against all-full."""
     import numpy as np
     import torch
 
@@ -646,34 +722,82 @@ def bench_hybrid256k(args):
     n_sa = float(sa_n.sum().item())
     by = sum((B * Hkv * nb if m_ else n_sa) * kv_block for m_ in mask) + len(mask) * B * Hq * d * 6
     by_f = len(mask) * B * Hkv * nb * kv_block + len(mask) * B * Hq * d * 6
-    _line(args, "routed hybrid decode HBM GB/s, 36 layers, 256K ctx, batch 1", by / (ms_h * 1e-3) / 1e9, "GB/s",
-          ms_h, {"workload": "one decode step through a 36-layer routed stack (18 full / 18 sink+window), "
-                             f"256K context, batch 1, 32 q / 8 kv heads, d 128, bf16 KV; full layers as 8 "
-                             f"context shards x {sps} splits", "batch": B, "context": L, "splits_per_shard": sps,
-                             "sa_splits": sas, "parallelism": "single-gpu"},
-          tokens_per_s=round(B / (ms_h * 1e-3), 2), all_full_ms=round(ms_f, 4),
-          all_full_gbs=round(by_f / (ms_f * 1e-3) / 1e9, 1), speedup_vs_all_full=round(ms_f / ms_h, 3),
-          byte_ratio=round(by_f / by, 3))
+    del qs, ks, vs, outs
+    torch.cuda.empty_cache()
+    return dict(workload="one decode step through a 36-layer routed stack (18 full / 18 sink+window), 256K context, "
+                         f"batch 1, 32 q / 8 kv heads, d 128, bf16 KV; full layers as 8 context shards x {sps} splits",
+                batch=B, context=L, splits_per_shard=sps, sa_splits=sas, ms=ms_h, bytes=by,
+                gbs=by / (ms_h * 1e-3) / 1e9, pct_peak=100 * by / (ms_h * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                tokens_per_s=B / (ms_h * 1e-3), all_full_ms=ms_f, all_full_gbs=by_f / (ms_f * 1e-3) / 1e9,
+                speedup_vs_all_full=ms_f / ms_h, byte_ratio=by_f / by)
+
+
+def bench_hybrid256k(args):
+    r = run_hybrid256k(args)
+    _line(args, "routed hybrid decode HBM GB/s, 36 layers, 256K ctx, batch 1", r["gbs"], "GB/s", r["ms"],
+          {"workload": r["workload"], "batch": r["batch"], "context": r["context"],
+           "splits_per_shard": r["splits_per_shard"], "sa_splits": r["sa_splits"], "parallelism": "single-gpu"},
+          tokens_per_s=round(r["tokens_per_s"], 2), all_full_ms=round(r["all_full_ms"], 4),
+          all_full_gbs=round(r["all_full_gbs"], 1), speedup_vs_all_full=round(r["speedup_vs_all_full"], 3),
+          byte_ratio=round(r["byte_ratio"], 3))
+
+
+def run_ceiling(reps=10):
+    """The achievable HBM read rate: the streaming-read probe (libsparse_kv_bench.so) over 4 GiB, for a
+    few grid sizes; the best median."""
+    import ctypes
+
+    import torch
+
+    from sparse_kv_amd import build
+
+    lib = ctypes.CDLL(build.BENCH_LIB)
+    f = lib.skv_bench_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    nbytes = 4 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(2048 * 256, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sweep = {}
+    for wgs in (512, 1024, 2048):
+        t = _timer()
+        for i in range(reps + 2):
+            with (t if i >= 2 else _timer()):
+                rc = f(ctypes.c_void_p(buf.data_ptr()), nbytes, wgs, ctypes.c_void_p(sink.data_ptr()), stream)
+                if rc != 0:
+                    raise RuntimeError(f"skv_bench_stream_read failed ({rc})")
+        sweep[wgs] = nbytes / (t.median_ms() * 1e-3) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    best = max(sweep, key=sweep.get)
+    return dict(kernel="stream_read_kernel (non-temporal 16-byte loads, whole lines)", bytes=nbytes,
+                gbs=sweep[best], pct_peak=100 * sweep[best] / PEAK_HBM_GBS, workgroups=best,
+                sweep_gbs={str(k_): round(v_, 1) for k_, v_ in sweep.items()})
 
 
 def cpu_baseline(inp, budget_s, topk, n_sink, n_recent, win_recent, tau, phi, patience, probe, bytes_per_unit):
-    """Time the float64 oracle on whole (batch row, KV head) units of the same input."""
+    """Time the float64 oracle on whole (batch row, KV head) units of the same input (every stage), with
+    numpy's BLAS threads as the process has them and with one thread; plus the small fp32 4K workload and
+    the 32K batch-8 dense workload, each with one thread and all threads."""
     import numpy as np
 
     import oracle
+    import synth
     from oracle.selection import forced_blocks
 
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
 
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = 1
+        import contextlib
+
+        cores, threadpool_limits = 1, lambda limits: contextlib.nullcontext()
     B, Hq, Hkv, d, L = inp.shape
     G = Hq // Hkv
-    done = 0
-    t0 = time.perf_counter()
-    for u in range(B * Hkv):
+
+    def step_unit(u):
         b, g = divmod(u, Hkv)
         qf = inp.upcast(inp.q[b:b + 1, g * G:(g + 1) * G])
         kf = inp.upcast(inp.k[b:b + 1, g:g + 1])
@@ -686,13 +810,62 @@ def cpu_baseline(inp, budget_s, topk, n_sink, n_recent, win_recent, tau, phi, pa
         oracle.art_decode(qf, kf, vf, seq, inp.scale, tau, phi, patience, probe)
         nb = -(-int(seq[0]) // 64)
         oracle.decode_blocks(qf, kf, vf, seq, inp.scale, [[sorted(forced_blocks(nb, n_sink, win_recent))]])
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": round(done * bytes_per_unit / el / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {B * Hkv} (batch row, KV head) units of the same input, every stage, "
-                      f"float64 numpy, {el:.1f}s"}
+
+    def timed(fn, items, budget):
+        done, t0 = 0, time.perf_counter()
+        for it in items:
+            fn(it)
+            done += 1
+            if time.perf_counter() - t0 > budget:
+                break
+        return done, time.perf_counter() - t0
+
+    done, el = timed(step_unit, range(B * Hkv), budget_s)
+    with threadpool_limits(limits=1):
+        done1, el1 = timed(step_unit, range(B * Hkv), budget_s / 3)
+    res = {"value": round(done * bytes_per_unit / el / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": f"{done} of {B * Hkv} (batch row, KV head) units of the same input, every stage, "
+                     f"float64 numpy, {el:.1f}s",
+           "single_thread": {"value": round(done1 * bytes_per_unit / el1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                             "sample": f"{done1} units, every stage, {el1:.1f}s"}}
+
+    # small fp32 single-head 4K workload: dense + top-8 (block 0 forced) selection + decode over it
+    W1 = synth.WORKLOADS[1]
+    t1 = synth.make_inputs(1, W1["B"], W1["Hq"], W1["Hkv"], W1["d"], W1["L"], dtype="f32", kind="gauss")
+    q1, k1, v1 = t1.f64()
+
+    def tiny(_):
+        oracle.decode_dense(q1, k1, v1, t1.seq_lens, t1.scale)
+        sig = oracle.centroid_scores(q1, oracle.block_centroids(k1, t1.seq_lens), t1.seq_lens, t1.scale)
+        oracle.decode_blocks(q1, k1, v1, t1.seq_lens, t1.scale,
+                             oracle.select_all(sig, t1.seq_lens, W1["topk"], W1["n_sink"], W1["n_recent"]))
+
+    # 32K batch-8 dense: 8 units drawn on their own (the same values as the GPU's input), before timing
+    W2 = synth.WORKLOADS[2]
+    G2 = W2["Hq"] // W2["Hkv"]
+    up = lambda a: synth.bf16_to_f32(a).astype(np.float64)
+    units2 = [tuple(up(x) for x in synth.draw_unit(2, b, 0, G2, W2["d"], W2["L"], W2["L"], "bf16", W2["kind"]))
+              for b in range(8)]
+
+    def dense32k(u):
+        qg, kk, vv = units2[u]
+        oracle.decode_dense(qg[None], kk[None, None], vv[None, None], np.array([W2["L"]], dtype=np.int32),
+                            1 / math.sqrt(W2["d"]))
+
+    for name, fn, n, by in (("tiny4k", tiny, 20, W1["L"] * W1["d"] * 4 * 2),
+                            ("dense32k_b8", dense32k, 8, W2["L"] * W2["d"] * 2 * 2)):
+        row = {}
+        for label, lim in (("threads", None), ("single_thread", 1)):
+            if lim is None:
+                k_, e_ = timed(fn, range(n), budget_s / 3)
+            else:
+                with threadpool_limits(limits=lim):
+                    k_, e_ = timed(fn, range(n), budget_s / 3)
+            row[label] = {"ms_per_item": round(1e3 * e_ / k_, 3), "gbs": round(k_ * by / e_ / 1e9, 4),
+                          "items": k_}
+        row["item"] = "one decode step" if name == "tiny4k" else "one (batch row, KV head) unit, dense"
+        res[name] = row
+    return res
 
 
 if __name__ == "__main__":

@@ -19,6 +19,9 @@ INC = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_kv.so")
 SOURCES = ["api.hip", "decode.hip", "merge.hip", "select.hip", "art.hip"]
+# the benchmark's streaming-read probe, a library of its own
+BENCH_LIB = os.path.join(HERE, "libsparse_kv_bench.so")
+BENCH_SOURCES = ["bench_read.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of the generated code on purpose.
@@ -48,21 +51,24 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
-    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
+    srcs = SOURCES + BENCH_SOURCES
+    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in srcs]
 
     def compile_one(i):
-        out = _run([cc, *CFLAGS, "-c", os.path.join(SRC, SOURCES[i]), "-o", objs[i]])
+        out = _run([cc, *CFLAGS, "-c", os.path.join(SRC, srcs[i]), "-o", objs[i]])
         if verbose and out.strip():
             print(out)
 
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
+    jobs = jobs or min(len(srcs), os.cpu_count() or 1, 16)
     with ThreadPoolExecutor(jobs) as ex:
-        list(ex.map(compile_one, range(len(SOURCES))))
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
+        list(ex.map(compile_one, range(len(srcs))))
+    for lib, n in ((LIB, len(SOURCES)), (BENCH_LIB, len(BENCH_SOURCES))):
+        tmp = lib + ".tmp"
+        part = objs[:n] if lib == LIB else objs[len(SOURCES):]
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *part, "-o", tmp])
+        os.replace(tmp, lib)
+        if verbose:
+            print("built", lib)
     return LIB
 
 
