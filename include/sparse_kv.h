@@ -4,9 +4,11 @@
  *
  * C ABI.  Every pointer argument is a DEVICE pointer unless its comment says
  * "host".  The caller owns every buffer; the library never allocates, frees
- * or synchronises, keeps no global state, and queues all work on `stream`
- * (a hipStream_t passed as void*; NULL = the default stream).  Functions are
- * reentrant and may be called concurrently on different streams.
+ * or synchronises, and queues all work on `stream` (a hipStream_t passed as
+ * void*; NULL = the default stream).  Its only global state is the scratch
+ * array of attn_decode_routed_static.  Functions are reentrant and may be
+ * called concurrently on different streams (attn_decode_routed_static: see
+ * there).
  *
  * Errors: every function returns an attn_status.  Host-visible arguments
  * (pointers for NULL, sizes, dims) are checked before anything is queued;
@@ -393,6 +395,28 @@ int attn_decode_routed(const attn_dims* dims, int32_t n_layers, const uint8_t* r
  * (0 on invalid arguments). */
 size_t attn_routed_workspace_bytes(const attn_dims* dims, int32_t n_shards,
                                    int32_t splits_per_shard, int32_t sa_splits);
+
+/*
+ * attn_decode_routed for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments, results and errors, without
+ * the workspace.  The split and shard states live in a scratch array of
+ * ATTN_ROUTED_STATIC_BYTES that the library holds on every device it runs on
+ * until the process ends; the call allocates nothing.
+ * ATTN_ERR_WORKSPACE when attn_routed_workspace_bytes() for the same
+ * arguments exceeds ATTN_ROUTED_STATIC_BYTES (nothing is queued).
+ * Every call on one device uses that device's one array, and the array keeps
+ * the last call's contents (no call reads a state it has not written): calls
+ * that overlap on one device -- other streams, other threads -- race.
+ * The first call on a device takes the array's address with that device made
+ * current for the duration (ATTN_ERR_HIP if that fails).
+ */
+#define ATTN_ROUTED_STATIC_BYTES (8u << 20)
+int attn_decode_routed_static(const attn_dims* dims, int32_t n_layers, const uint8_t* route_mask,
+                              const void* const* q, const void* const* k, const void* const* v,
+                              const int32_t* seq_lens, int32_t n_shards, int32_t splits_per_shard,
+                              const int32_t* sa_block_idx, const int32_t* sa_n_sel, int32_t sa_max_sel,
+                              int32_t sa_splits, float* const* out, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* attn_status_string(int status);

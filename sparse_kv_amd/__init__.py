@@ -48,6 +48,7 @@ EXPORTS = (
     "attn_decode_art_paged",
     "attn_decode_routed",
     "attn_routed_workspace_bytes",
+    "attn_decode_routed_static",
     "attn_status_string",
 )
 
@@ -104,7 +105,9 @@ _SIG = {
     "attn_decode_art_paged": [_D, _P, _K, _P, _P, _F, _F, _I, _I, _P, _P, _P, _P],
     "attn_decode_routed": [_D, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _P, ctypes.c_size_t, _P, _P],
     "attn_routed_workspace_bytes": [_D, _I, _I, _I],
+    "attn_decode_routed_static": [_D, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P],
 }
+ROUTED_STATIC_BYTES = 8 << 20  # ATTN_ROUTED_STATIC_BYTES
 _lib = None
 
 
@@ -565,19 +568,11 @@ def attn_routed_workspace_bytes(q, k, n_shards=8, splits_per_shard=4, sa_splits=
                                                 int(sa_splits)))
 
 
-def attn_decode_routed(qs, ks, vs, route_mask, seq_lens=None, n_shards=8, splits_per_shard=4,
-                       sa_block_idx=None, sa_n_sel=None, sa_splits=4, workspace=None, outs=None,
-                       scale=None):
-    """One decode step of a layer stack under a per-layer hard route mask.
-
-    qs, ks, vs: per-layer tensors of one shape; route_mask: sequence of 0/1
-    (1 = full attention).  Returns the list of per-layer outputs [B, Hq, d].
-    """
+def _routed_args(qs, ks, vs, route_mask, seq_lens, outs, scale):
+    """Checked (dims, device, seq, outs, C arrays) shared by the routed entry points."""
     n = len(qs)
     if not (len(ks) == len(vs) == len(route_mask) == n):
         raise ValueError("qs, ks, vs and route_mask must have one entry per layer")
-    if n == 0:
-        return []
     dev = qs[0].device
     dims = _dims_from(qs[0], ks[0], scale)
     for i in range(n):
@@ -588,28 +583,57 @@ def attn_decode_routed(qs, ks, vs, route_mask, seq_lens=None, n_shards=8, splits
     if outs is None:
         outs = [torch.empty((dims.batch, dims.num_q_heads, dims.head_dim), dtype=torch.float32, device=dev)
                 for _ in range(n)]
+    if len(outs) != n:
+        raise ValueError("outs must have one entry per layer")
     for i, t in enumerate(outs):
         _need(t, f"outs[{i}]", dev, torch.float32, (dims.batch, dims.num_q_heads, dims.head_dim))
+    mask = (ctypes.c_uint8 * n)(*[1 if int(x) else 0 for x in route_mask])
+    arr = ctypes.c_void_p * n
+    ptrs = [ctypes.cast(a, _P) for a in (arr(*[t.data_ptr() for t in qs]), arr(*[t.data_ptr() for t in ks]),
+                                           arr(*[t.data_ptr() for t in vs]), arr(*[t.data_ptr() for t in outs]))]
+    return dims, dev, seq, outs, ctypes.cast(mask, _P), ptrs, (mask,)
+
+
+def attn_decode_routed(qs, ks, vs, route_mask, seq_lens=None, n_shards=8, splits_per_shard=4,
+                       sa_block_idx=None, sa_n_sel=None, sa_splits=4, workspace=None, outs=None,
+                       scale=None):
+    """One decode step of a layer stack under a per-layer hard route mask.
+
+    qs, ks, vs: per-layer tensors of one shape; route_mask: sequence of 0/1
+    (1 = full attention).  Returns the list of per-layer outputs [B, Hq, d].
+    """
+    if len(qs) == 0:
+        return []
+    dims, dev, seq, outs, mask, (qa, ka, va, oa), keep = _routed_args(qs, ks, vs, route_mask, seq_lens, outs, scale)
     need = int(lib().attn_routed_workspace_bytes(ctypes.byref(dims), int(n_shards), int(splits_per_shard),
                                                 int(sa_splits)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", dev)
-    mask = (ctypes.c_uint8 * n)(*[1 if int(x) else 0 for x in route_mask])
-    arr = ctypes.c_void_p * n
-    qa = arr(*[t.data_ptr() for t in qs])
-    ka = arr(*[t.data_ptr() for t in ks])
-    va = arr(*[t.data_ptr() for t in vs])
-    oa = arr(*[t.data_ptr() for t in outs])
     max_sel = int(sa_block_idx.shape[-1]) if sa_block_idx is not None else 0
     with _on_device(dev):
-        st = lib().attn_decode_routed(ctypes.byref(dims), n, ctypes.cast(mask, _P), ctypes.cast(qa, _P),
-                                     ctypes.cast(ka, _P), ctypes.cast(va, _P), _ptr(seq), int(n_shards),
+        st = lib().attn_decode_routed(ctypes.byref(dims), len(qs), mask, qa, ka, va, _ptr(seq), int(n_shards),
                                      int(splits_per_shard), _ptr(sa_block_idx), _ptr(sa_n_sel), max_sel,
                                      int(sa_splits), _ptr(workspace),
-                                     workspace.numel() * workspace.element_size(), ctypes.cast(oa, _P),
-                                     _stream(dev))
+                                     workspace.numel() * workspace.element_size(), oa, _stream(dev))
     _check(st, "attn_decode_routed")
+    return outs
+
+
+def attn_decode_routed_static(qs, ks, vs, route_mask, seq_lens=None, n_shards=8, splits_per_shard=4,
+                              sa_block_idx=None, sa_n_sel=None, sa_splits=4, outs=None, scale=None):
+    """attn_decode_routed without a workspace: the library's own static device scratch
+    (ROUTED_STATIC_BYTES per device) holds the states; the C call allocates nothing
+    (pass `outs` to allocate nothing here either).  Overlapping calls on one device race."""
+    if len(qs) == 0:
+        return []
+    dims, dev, seq, outs, mask, (qa, ka, va, oa), keep = _routed_args(qs, ks, vs, route_mask, seq_lens, outs, scale)
+    max_sel = int(sa_block_idx.shape[-1]) if sa_block_idx is not None else 0
+    with _on_device(dev):
+        st = lib().attn_decode_routed_static(ctypes.byref(dims), len(qs), mask, qa, ka, va, _ptr(seq),
+                                            int(n_shards), int(splits_per_shard), _ptr(sa_block_idx),
+                                            _ptr(sa_n_sel), max_sel, int(sa_splits), oa, _stream(dev))
+    _check(st, "attn_decode_routed_static")
     return outs
 
 

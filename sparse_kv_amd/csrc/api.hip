@@ -1,12 +1,21 @@
 // C ABI of the decode-attention library: argument checks and kernel dispatch.
-// Host code only; every kernel is queued on the caller's stream and nothing
-// here allocates, frees or synchronises.
+// Every kernel is queued on the caller's stream and nothing here allocates,
+// frees or synchronises.  The one piece of device state is the static scratch
+// array of attn_decode_routed_static (with its per-device address cache).
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
 #include "sparse_kv.h"
+
+// Scratch of attn_decode_routed_static: one copy per device, for the life of
+// the process.  Host code never uses the array's name as an address (on the
+// host it is only a handle to the symbol); each device's address is taken
+// once, with that device current, and kept (static_scratch below).
+static __device__ __align__(256) char scratch[ATTN_ROUTED_STATIC_BYTES];
 
 namespace {
 
@@ -97,6 +106,97 @@ void set_paged(skv::DecodeArgs& a, const attn_paged_kv* kv) {
   a.table = kv->block_table;
   a.table_stride = kv->table_stride;
   a.pool_blocks = kv->pool_blocks;
+}
+
+// Host-side checks shared by the routed entry points (nothing is queued on failure).
+int routed_check(const attn_dims* dims, int32_t n_layers, const uint8_t* route_mask, const void* const* q,
+                 const void* const* k, const void* const* v, int32_t n_shards, int32_t splits_per_shard,
+                 const int32_t* sa_block_idx, const int32_t* sa_n_sel, int32_t sa_max_sel, int32_t sa_splits,
+                 float* const* out) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (n_layers < 0 || !route_mask || !q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
+  if (n_shards < 1 || splits_per_shard < 1 || sa_splits < 1 || sa_splits > (1 << 24)) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)n_shards * splits_per_shard > (1 << 24)) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)dims->batch * dims->num_q_heads * n_shards > 0x7fffffff) return ATTN_ERR_INVALID_ARG;
+  bool any_sa = false;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    if (!q[i] || !k[i] || !v[i] || !out[i]) return ATTN_ERR_INVALID_ARG;
+    any_sa |= route_mask[i] == 0;
+  }
+  if (any_sa && (!sa_block_idx || !sa_n_sel || sa_max_sel < 1)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+// The layers of a routed stack, queued in order; ws holds routed_layout's buffers.
+int routed_run(const attn_dims* dims, int32_t n_layers, const uint8_t* route_mask, const void* const* q,
+               const void* const* k, const void* const* v, const int32_t* seq_lens, int32_t n_shards,
+               int32_t splits_per_shard, const int32_t* sa_block_idx, const int32_t* sa_n_sel, int32_t sa_max_sel,
+               int32_t sa_splits, char* ws, float* const* out, hipStream_t s) {
+  if (dims->batch == 0 || n_layers == 0) return ATTN_OK;
+  const RoutedLayout lay = routed_layout(dims, n_shards, splits_per_shard, sa_splits);
+  float* m = (float*)(ws + lay.m);
+  float* l = (float*)(ws + lay.l);
+  float* o = (float*)(ws + lay.o);
+  float* sm = (float*)(ws + lay.sm);
+  float* sl = (float*)(ws + lay.sl);
+  float* so = (float*)(ws + lay.so);
+  const int32_t rows = dims->batch * dims->num_q_heads;
+  const int32_t S = n_shards * splits_per_shard;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    hipError_t e;
+    if (route_mask[i]) {
+      // full attention: shard-aligned splits, merged per shard, then across shards
+      skv::DecodeArgs a = decode_args(dims, q[i], k[i], v[i], seq_lens, S, m, l, o);
+      e = skv::launch_decode(a, false, s);
+      if (e == hipSuccess)
+        e = skv::launch_merge(rows * n_shards, splits_per_shard, dims->head_dim, m, l, o, so, sm, sl, s);
+      if (e == hipSuccess) e = skv::launch_merge(rows, n_shards, dims->head_dim, sm, sl, so, out[i], nullptr, nullptr, s);
+    } else {
+      skv::DecodeArgs a = decode_args(dims, q[i], k[i], v[i], seq_lens, sa_splits, m, l, o);
+      a.block_idx = sa_block_idx;
+      a.n_sel = sa_n_sel;
+      a.max_sel = sa_max_sel;
+      e = skv::launch_decode(a, true, s);
+      if (e == hipSuccess) e = skv::launch_merge(rows, sa_splits, dims->head_dim, m, l, o, out[i], nullptr, nullptr, s);
+    }
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+char* scratch_ptr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+// The device that work queued on `s` runs on.
+int stream_device(hipStream_t s, int* dev) {
+  const hipError_t e = s ? hipStreamGetDevice(s, dev) : hipGetDevice(dev);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  return *dev >= 0 && *dev < kMaxDevices ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
+}
+
+int static_scratch(hipStream_t s, char** ptr) {
+  int dev = 0;
+  int st = stream_device(s, &dev);
+  if (st) return st;
+  std::call_once(scratch_once[dev], [dev] {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    scratch_err[dev] = e;
+    scratch_ptr[dev] = e == hipSuccess ? (char*)p : nullptr;
+  });
+  if (scratch_err[dev] != hipSuccess || !scratch_ptr[dev]) return ATTN_ERR_HIP;
+  *ptr = scratch_ptr[dev];
+  return ATTN_OK;
 }
 
 }  // namespace
@@ -448,53 +548,30 @@ int attn_decode_routed(const attn_dims* dims, int32_t n_layers, const uint8_t* r
                        const int32_t* sa_block_idx, const int32_t* sa_n_sel, int32_t sa_max_sel,
                        int32_t sa_splits, void* workspace, size_t workspace_bytes,
                        float* const* out, void* stream) {
-  int st = check_dims(dims);
+  int st = routed_check(dims, n_layers, route_mask, q, k, v, n_shards, splits_per_shard, sa_block_idx, sa_n_sel,
+                        sa_max_sel, sa_splits, out);
   if (st) return st;
-  if (n_layers < 0 || !route_mask || !q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
-  if (n_shards < 1 || splits_per_shard < 1 || sa_splits < 1 || sa_splits > (1 << 24)) return ATTN_ERR_INVALID_ARG;
-  if ((int64_t)n_shards * splits_per_shard > (1 << 24)) return ATTN_ERR_INVALID_ARG;
-  if ((int64_t)dims->batch * dims->num_q_heads * n_shards > 0x7fffffff) return ATTN_ERR_INVALID_ARG;
-  bool any_sa = false;
-  for (int32_t i = 0; i < n_layers; ++i) {
-    if (!q[i] || !k[i] || !v[i] || !out[i]) return ATTN_ERR_INVALID_ARG;
-    any_sa |= route_mask[i] == 0;
-  }
-  if (any_sa && (!sa_block_idx || !sa_n_sel || sa_max_sel < 1)) return ATTN_ERR_INVALID_ARG;
   if (!workspace) return ATTN_ERR_INVALID_ARG;
-  const RoutedLayout lay = routed_layout(dims, n_shards, splits_per_shard, sa_splits);
-  if (workspace_bytes < lay.total) return ATTN_ERR_WORKSPACE;
-  if (dims->batch == 0 || n_layers == 0) return ATTN_OK;
+  if (workspace_bytes < routed_layout(dims, n_shards, splits_per_shard, sa_splits).total) return ATTN_ERR_WORKSPACE;
+  return routed_run(dims, n_layers, route_mask, q, k, v, seq_lens, n_shards, splits_per_shard, sa_block_idx,
+                    sa_n_sel, sa_max_sel, sa_splits, (char*)workspace, out, (hipStream_t)stream);
+}
 
-  char* ws = (char*)workspace;
-  float* m = (float*)(ws + lay.m);
-  float* l = (float*)(ws + lay.l);
-  float* o = (float*)(ws + lay.o);
-  float* sm = (float*)(ws + lay.sm);
-  float* sl = (float*)(ws + lay.sl);
-  float* so = (float*)(ws + lay.so);
-  const hipStream_t s = (hipStream_t)stream;
-  const int32_t rows = dims->batch * dims->num_q_heads;
-  const int32_t S = n_shards * splits_per_shard;
-  for (int32_t i = 0; i < n_layers; ++i) {
-    hipError_t e;
-    if (route_mask[i]) {
-      // full attention: shard-aligned splits, merged per shard, then across shards
-      skv::DecodeArgs a = decode_args(dims, q[i], k[i], v[i], seq_lens, S, m, l, o);
-      e = skv::launch_decode(a, false, s);
-      if (e == hipSuccess)
-        e = skv::launch_merge(rows * n_shards, splits_per_shard, dims->head_dim, m, l, o, so, sm, sl, s);
-      if (e == hipSuccess) e = skv::launch_merge(rows, n_shards, dims->head_dim, sm, sl, so, out[i], nullptr, nullptr, s);
-    } else {
-      skv::DecodeArgs a = decode_args(dims, q[i], k[i], v[i], seq_lens, sa_splits, m, l, o);
-      a.block_idx = sa_block_idx;
-      a.n_sel = sa_n_sel;
-      a.max_sel = sa_max_sel;
-      e = skv::launch_decode(a, true, s);
-      if (e == hipSuccess) e = skv::launch_merge(rows, sa_splits, dims->head_dim, m, l, o, out[i], nullptr, nullptr, s);
-    }
-    if (e != hipSuccess) return ATTN_ERR_HIP;
-  }
-  return ATTN_OK;
+int attn_decode_routed_static(const attn_dims* dims, int32_t n_layers, const uint8_t* route_mask,
+                              const void* const* q, const void* const* k, const void* const* v,
+                              const int32_t* seq_lens, int32_t n_shards, int32_t splits_per_shard,
+                              const int32_t* sa_block_idx, const int32_t* sa_n_sel, int32_t sa_max_sel,
+                              int32_t sa_splits, float* const* out, void* stream) {
+  int st = routed_check(dims, n_layers, route_mask, q, k, v, n_shards, splits_per_shard, sa_block_idx, sa_n_sel,
+                        sa_max_sel, sa_splits, out);
+  if (st) return st;
+  if (routed_layout(dims, n_shards, splits_per_shard, sa_splits).total > ATTN_ROUTED_STATIC_BYTES)
+    return ATTN_ERR_WORKSPACE;
+  if (dims->batch == 0 || n_layers == 0) return ATTN_OK;
+  char* ws = nullptr;
+  if ((st = static_scratch((hipStream_t)stream, &ws))) return st;
+  return routed_run(dims, n_layers, route_mask, q, k, v, seq_lens, n_shards, splits_per_shard, sa_block_idx,
+                    sa_n_sel, sa_max_sel, sa_splits, ws, out, (hipStream_t)stream);
 }
 
 }  // extern "C"

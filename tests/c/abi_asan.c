@@ -1,5 +1,5 @@
 /* Drives the C-ABI layer (argument checks, workspace layouts, the routed
- * layer loop) against the
+ * layer loop, the static scratch of attn_decode_routed_static) against the
  * recording launchers of launch_stubs.cpp, under the host address and
  * undefined-behaviour sanitizers.  No GPU: nothing here reaches a kernel.
  * Prints "ok" and exits 0 when every check holds. */
@@ -13,7 +13,9 @@
 extern int stub_launches;
 extern const void* stub_last_ptr[4];
 extern int stub_last_S;
+extern int stub_device_count;
 void stub_reset(void);
+int hipSetDevice(int);
 
 static int fails = 0;
 #define CHECK(cond)                                                       \
@@ -125,6 +127,38 @@ int main(void) {
     CHECK(attn_decode_routed(&d, 3, mask, ptrs, ptrs, ptrs, NULL, 8, 2, fi, fi, 4, 4, ws, need - 1, outs, NULL) ==
           ATTN_ERR_WORKSPACE);
     free(ws);
+
+    /* the same without a workspace: one static scratch, the same on every call;
+       the first call on a second device takes that device's address */
+    {
+      const void* first[3];
+      stub_reset();
+      CHECK(attn_decode_routed_static(&d, 3, mask, ptrs, ptrs, ptrs, NULL, 8, 2, fi, fi, 4, 4, outs, NULL) ==
+            ATTN_OK);
+      CHECK(stub_launches == 8);
+      for (i = 0; i < 3; ++i) {
+        first[i] = stub_last_ptr[i];
+        CHECK(first[i] != NULL && ((uintptr_t)first[i] & 255) == 0);
+      }
+      stub_device_count = 2;
+      CHECK(hipSetDevice(1) == 0);
+      stub_reset();
+      CHECK(attn_decode_routed_static(&d, 3, mask, ptrs, ptrs, ptrs, NULL, 8, 2, fi, fi, 4, 4, outs, NULL) ==
+            ATTN_OK);
+      for (i = 0; i < 3; ++i) CHECK(stub_last_ptr[i] == first[i]);
+      CHECK(hipSetDevice(0) == 0);
+      /* states beyond the scratch: refused before anything is queued */
+      {
+        attn_dims big = dims(64, 32, 8, 128, 4);
+        CHECK(attn_routed_workspace_bytes(&big, 8, 4, 4) > ATTN_ROUTED_STATIC_BYTES);
+        stub_reset();
+        CHECK(attn_decode_routed_static(&big, 3, mask, ptrs, ptrs, ptrs, NULL, 8, 4, fi, fi, 4, 4, outs, NULL) ==
+              ATTN_ERR_WORKSPACE);
+        CHECK(stub_launches == 0);
+      }
+      CHECK(attn_decode_routed_static(&d, 3, mask, ptrs, ptrs, ptrs, NULL, 8, 2, NULL, fi, 4, 4, outs, NULL) ==
+            ATTN_ERR_INVALID_ARG);
+    }
   }
   free(fake);
   if (fails == 0) printf("ok\n");

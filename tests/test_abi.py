@@ -165,6 +165,18 @@ def test_routed_workspace_and_validation(skv):
                                     ctypes.cast(ptrs, P), ctypes.cast(ptrs, P), None, 8, 2, FAKE, FAKE, 4,
                                     (1 << 24) + 1, FAKE, 1 << 40, ctypes.cast(ptrs, P), None)
     assert big_sa == -1  # split counts are bounded
+    # the workspace-free variant: the same checks, then the states must fit its static scratch
+    stat = lambda dd, ns, sps, sas, sa=FAKE, n=2: lib.attn_decode_routed_static(
+        ctypes.byref(dd), n, ctypes.cast(mask, P), ctypes.cast(ptrs, P), ctypes.cast(ptrs, P), ctypes.cast(ptrs, P),
+        None, ns, sps, sa, FAKE, 4, sas, ctypes.cast(ptrs, P), None)
+    assert stat(d, 8, 2, 4, sa=None) == -1
+    assert stat(d, 0, 2, 4) == -1
+    assert stat(dims(head_dim=96), 8, 2, 4) == -2
+    big_d = dims(batch=64, num_q_heads=32, num_kv_heads=8)
+    assert lib.attn_routed_workspace_bytes(ctypes.byref(big_d), 8, 4, 4) > skv.ROUTED_STATIC_BYTES
+    assert stat(big_d, 8, 4, 4) == -4  # refused before anything touches a device
+    assert stat(dims(batch=0), 8, 2, 4) == 0
+    assert stat(d, 8, 2, 4, n=0) == 0
 
 
 def test_art_workspace_and_validation(skv):

@@ -1,5 +1,6 @@
 """The C-ABI layer (sparse_kv_amd/csrc/api.hip: argument checks, workspace
-layouts, the routed layer loop) built for the host with the address and undefined-behaviour
+layouts, the routed layer loop, the static scratch of the workspace-free
+routed call) built for the host with the address and undefined-behaviour
 sanitizers, linked against recording stand-ins of the kernel launchers
 (tests/c/launch_stubs.cpp) and driven from C (tests/c/abi_asan.c).  CPU only."""
 
@@ -17,7 +18,8 @@ def test_abi_layer_under_host_sanitizers(tmp_path):
     cxx, cc = shutil.which("g++"), shutil.which("gcc")
     if not cxx or not cc or not os.path.isdir(ROCM_INC):
         pytest.skip("needs g++, gcc and the ROCm headers")
-    # the layer is plain host code; it is compiled as C++ from a copy named .cpp
+    # the layer is plain host code apart from the scratch array's declaration;
+    # it is compiled as C++ from a copy named .cpp
     src = tmp_path / "api_host.cpp"
     shutil.copyfile(os.path.join(ROOT, "sparse_kv_amd", "csrc", "api.hip"), src)
     san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g", "-O1"]
