@@ -291,9 +291,10 @@ int attn_decode_art(const attn_dims* dims, const void* q, const void* k, const v
  * attn_decode_art with a workspace, for batches too small to fill the chip.
  * Defines: as attn_decode_art ("ART (Attention Run-time Termination)"
  * summary, §2.1-2.4); same arguments, results and errors.  With
- * B * Hkv <= 128 and at least 2 CUs per (b, kv head) on the current device,
- * each (b, kv head) is streamed by up to 4 workgroups on different CUs that
- * hand block states to per-head folding waves through the workspace;
+ * B * Hkv <= 128 and at least 2 CUs per (b, kv head) on the device of
+ * `stream`, each (b, kv head) is streamed by up to 4 workgroups on different
+ * CUs that hand block states to folding waves through the workspace, and as
+ * CUs free up further workgroups join the (b, kv heads) still running;
  * read-ahead past the stop is then at most max(64, T + 1) blocks, and at
  * most 128, per KV head.  Otherwise it runs as attn_decode_art and the
  * workspace is not touched.

@@ -30,11 +30,14 @@
 // always has its slot free.  Producers leave when the folder signals done.
 //
 // With fewer (b, kv head) units than half the CUs, a second form spreads each
-// unit over up to 4 workgroups (art_mc_kernel below): the ring moves to a
-// caller-provided workspace in device memory (128 slots, device-scope
+// unit over up to 4 workgroups (art_mc_kernel below), with further
+// workgroups joining the units still running as CUs free up: the ring moves
+// to a caller-provided workspace in device memory (128 slots, device-scope
 // accesses), producers claim visit positions from a per-unit counter, and
 // four folder waves (one per query head, or per two heads when G > 4) fold
-// batches of up to 64 (32) positions.
+// batches of up to 64 (32) positions; with one head per wave a batch's
+// running states come from wave-wide DPP prefix sums against one reference
+// max.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -149,7 +152,7 @@ struct GlobalRing {
   // control words, on separate 128-byte lines: the folders' counts of
   // folded positions (polled by every producer), the position claims, the
   // accounting words
-  enum Ctrl { kFolded = 0, kNext = 32, kFetched = 64, kExited, kFolder, kNumCtrl = 96 };
+  enum Ctrl { kFolded = 0, kNext = 32, kFetched = 64, kFolder, kNumCtrl = 96 };
   static_assert(NF <= 8 && R * 4 <= 512, "control and position areas");
   static constexpr uint32_t kPosOff = 0, kCtrlOff = 512;
   static constexpr uint32_t kMOff = kCtrlOff + 512;
@@ -527,8 +530,24 @@ template <int K, int CH>
 __device__ __forceinline__ float shr(float x) {
   if constexpr (CH <= 16)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + K, 0xF, 0xF, false));
+  else if constexpr (CH == 64 && K == 1)  // wave_shr:1 (lane 0 gets 0)
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x138, 0xF, 0xF, false));
   else
     return __shfl(x, ((int)threadIdx.x - K) & 63);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, all in DPP: row_shr 1, 2,
+// 4, 8 within rows of 16 (lanes whose source lies in the previous row add 0),
+// then row_bcast:15 adds row 0's total to row 1 and row 2's to row 3, and
+// row_bcast:31 adds the first 32 lanes' total to rows 2 and 3.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
+  return x;
 }
 
 // One inclusive-scan step over groups of CH lanes: lanes at group position
@@ -542,6 +561,34 @@ __device__ __forceinline__ void scan_step(int j, float& m, float& l, float (&a)[
     for (int k = 0; k < PW; ++k) ae[k] = shr<K, CH>(a[k]);
     if (j >= K) merge_into<PW>(me, le, ae, m, l, a);
   }
+}
+
+// One inclusive prefix-sum step over groups of CH lanes.
+template <int K, int CH, int PW>
+__device__ __forceinline__ void sum_step(int j, float& l, float (&a)[PW]) {
+  if constexpr (K < CH) {
+    const float le = shr<K, CH>(l);
+    float ae[PW];
+#pragma unroll
+    for (int k = 0; k < PW; ++k) ae[k] = shr<K, CH>(a[k]);
+    if (j >= K) {
+      l += le;
+#pragma unroll
+      for (int k = 0; k < PW; ++k) a[k] += ae[k];
+    }
+  }
+}
+
+// Maximum over each group of CH consecutive lanes (8, 16, 32 or 64), in every lane.
+template <int CH>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror: groups of 8
+  if constexpr (CH >= 16) x = fmaxf(x, dpp<0x140>(x));  // row_mirror: groups of 16
+  if constexpr (CH >= 32) x = xrow16_max(x);
+  if constexpr (CH >= 64) x = xhalf_max(x);
+  return x;
 }
 
 // Probe of a state: norm n and unit direction u of the first P channels of
@@ -630,14 +677,47 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int f, int b, i
       }
     }
     const float mb = m;
-    scan_step<1, CH, PW>(j, m, l, a);
-    scan_step<2, CH, PW>(j, m, l, a);
-    scan_step<4, CH, PW>(j, m, l, a);
-    scan_step<8, CH, PW>(j, m, l, a);
-    scan_step<16, CH, PW>(j, m, l, a);
-    scan_step<32, CH, PW>(j, m, l, a);
-    // state after block j = carry (+) scan_j
-    merge_into<PW>(cM, cL, cA, m, l, a);
+    // The running state after every block of the batch.  Usually all of them
+    // are taken relative to one reference, the largest block max of the batch
+    // and the carry: each block's (l, a) scaled by exp2(m_j - Mref), then
+    // plain prefix sums.  That holds whenever the first running max is within
+    // 2^100 of Mref (so no running sum can underflow); otherwise the batch
+    // takes the online-softmax merge at every scan step.
+    const float Mref = fmaxf(group_max<CH>(mb), cM);
+    const float Mrs = Mref == -INFINITY ? 0.f : Mref;
+    const float first = fmaxf(cM, CH == 64 ? readlane(mb, 0) : __shfl(mb, hh * CH));
+    if (__ballot(!(first >= Mrs - 100.f) && live) == 0) {
+      const float wj = in ? fast_exp2(mb - Mrs) : 0.f;
+      l *= wj;
+#pragma unroll
+      for (int k = 0; k < PW; ++k) a[k] *= wj;
+      if constexpr (CH == 64) {
+        l = wave_prefix_sum(l);
+#pragma unroll
+        for (int k = 0; k < PW; ++k) a[k] = wave_prefix_sum(a[k]);
+      } else {
+        sum_step<1, CH, PW>(j, l, a);
+        sum_step<2, CH, PW>(j, l, a);
+        sum_step<4, CH, PW>(j, l, a);
+        sum_step<8, CH, PW>(j, l, a);
+        sum_step<16, CH, PW>(j, l, a);
+        sum_step<32, CH, PW>(j, l, a);
+      }
+      const float cw = cL > 0.f ? fast_exp2(cM - Mrs) : 0.f;
+      l = fmaf(cw, cL, l);
+#pragma unroll
+      for (int k = 0; k < PW; ++k) a[k] = fmaf(cw, cA[k], a[k]);
+      m = Mref;
+    } else {
+      scan_step<1, CH, PW>(j, m, l, a);
+      scan_step<2, CH, PW>(j, m, l, a);
+      scan_step<4, CH, PW>(j, m, l, a);
+      scan_step<8, CH, PW>(j, m, l, a);
+      scan_step<16, CH, PW>(j, m, l, a);
+      scan_step<32, CH, PW>(j, m, l, a);
+      // state after block j = carry (+) scan_j
+      merge_into<PW>(cM, cL, cA, m, l, a);
+    }
     float nrm, u[PW];
     probe_of<PW>(l, a, nrm, u);
     float cn, cu[PW];
@@ -667,13 +747,25 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int f, int b, i
     const bool hit = st && run >= p.patience;
     const uint64_t rowh = ((uint64_t)__ballot(hit) >> (hh * CH)) & RM;
     const int jend = rowh ? __builtin_ctzll(rowh) : n - 1;
-    const int src = hh * CH + jend;
-    // the new running state: the state at jend
-    const float nM = __shfl(m, src), nL = __shfl(l, src);
-    const int nrun = __shfl(run, src);
-    float nA[PW];
+    // the new running state: the state at jend (one lane for the whole wave
+    // when a wave folds one head)
+    float nM, nL, nA[PW];
+    int nrun;
+    if constexpr (CH == 64) {
+      const int src = __builtin_amdgcn_readfirstlane(jend);
+      nM = readlane(m, src);
+      nL = readlane(l, src);
+      nrun = __builtin_amdgcn_readlane(run, src);
 #pragma unroll
-    for (int k = 0; k < PW; ++k) nA[k] = k < P ? __shfl(a[k], src) : 0.f;
+      for (int k = 0; k < PW; ++k) nA[k] = k < P ? readlane(a[k], src) : 0.f;
+    } else {
+      const int src = hh * CH + jend;
+      nM = __shfl(m, src);
+      nL = __shfl(l, src);
+      nrun = __shfl(run, src);
+#pragma unroll
+      for (int k = 0; k < PW; ++k) nA[k] = k < P ? __shfl(a[k], src) : 0.f;
+    }
     // weights of the batch's blocks in the new state, staged for the output fold
     const float nMs = nM == -INFINITY ? 0.f : nM;
     fold_w[lane] = (in && j <= jend) ? fast_exp2(mb - nMs) : 0.f;
@@ -772,20 +864,28 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
 // on one CU is bound by that CU.  The unit's workgroups share a ring in
 // global memory; the first wave 0 to arrive folds, the other wave 0s leave,
 // and every producer wave claims positions from the unit's counter, so
-// progress never depends on which workgroups are resident.  The last
-// workgroup to finish reports the fetch count.
+// progress never depends on which workgroups are resident.  The grid holds
+// `groups` workgroups per unit, then late workgroups: each of those joins a
+// unit whose folders are still at work when it starts (units stop at very
+// different positions, and these add producers to the ones still running
+// once the early finishers have freed their CUs), or leaves if none is.
+// Every workgroup adds its fetch count to the unit's total on the way out
+// and raises the reported count to the total it saw, so the report ends as
+// the total whichever workgroup leaves last.
 template <int GP, int D, int R>
-__global__ __launch_bounds__(128) void art_ring_init(char* ws) {
+__global__ __launch_bounds__(128) void art_ring_init(char* ws, int32_t* blocks_fetched) {
   using RING = GlobalRing<GP, D, R, 4>;
   RING ring(ws, blockIdx.x);
   if (threadIdx.x < R) ring.pos[threadIdx.x] = -1;
   if (threadIdx.x < RING::kNumCtrl) ring.ctrl[threadIdx.x] = 0;
+  if (threadIdx.x == 0 && blocks_fetched) blocks_fetched[blockIdx.x] = 0;
 }
 
 template <typename T, int D, int GR, int NP>
 struct ArtMcShared : ArtWaves<T, D, GR, NP> {
   int fetched;
   int role;  // 0: this workgroup's first waves fold
+  int join;  // a late workgroup's unit (-1: every unit has finished)
 };
 
 template <typename T, int D, int GR, int NP, int R>
@@ -799,7 +899,33 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* 
   using RING = GlobalRing<4 * GR, D, R, NF, Geo<T, D>::E>;
   __shared__ SH sh;
   const int units = p.B * p.Hkv;
-  const int unit = blockIdx.x % units;
+  int unit = (int)blockIdx.x % units;
+  if ((int)blockIdx.x >= units * groups) {
+    // a late workgroup: the first unit, from its own on, whose folders have
+    // not all finished (units <= 128: two looks per lane at most)
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      int pick = -1;
+      for (int base = 0; base < units && pick < 0; base += 64) {
+        const int u = (unit + base + lane) % units;
+        bool active = false;
+        if (base + lane < units) {
+          RING r(ws, u);
+          int done = 0;
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            done += __hip_atomic_load(&r.ctrl[RING::kFolded + f], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= kDoneMark;
+          active = done < NF;
+        }
+        const uint64_t act = (uint64_t)__ballot(active);
+        if (act) pick = (unit + base + (int)__builtin_ctzll(act)) % units;
+      }
+      if (lane == 0) sh.join = pick;
+    }
+    __syncthreads();
+    if (sh.join < 0) return;  // the whole workgroup
+    unit = sh.join;
+  }
   const int b = unit / p.Hkv, g = unit % p.Hkv;
   const int w = threadIdx.x >> 6;
   const int G = p.Hq / p.Hkv;
@@ -823,14 +949,12 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* 
     art_producer<T, D, GR>(p, sh, ring, pos, __builtin_amdgcn_readfirstlane(w - 1), unit, b, g, G, L, nb, nv);
   }
   __syncthreads();
-  // the workgroup's fetch count is added (and complete) before it counts
-  // itself out; the last one out reads the unit's total
+  // the unit's running total including this workgroup's fetches; the report
+  // is raised to it (the caller's counts were zeroed by the ring reset)
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(&ring.ctrl[RING::kFetched], sh.fetched, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    RING::wait_memory();
-    const int before = __hip_atomic_fetch_add(&ring.ctrl[RING::kExited], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (before == groups - 1 && p.blocks_fetched)
-      p.blocks_fetched[unit] = __hip_atomic_load(&ring.ctrl[RING::kFetched], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int total = sh.fetched + __hip_atomic_fetch_add(&ring.ctrl[RING::kFetched], sh.fetched, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+    if (p.blocks_fetched) atomicMax(&p.blocks_fetched[unit], total);
   }
 }
 
@@ -840,10 +964,10 @@ constexpr size_t art_ring_bytes(int G) {
 }
 
 template <typename T, int D, int GR>
-hipError_t launch_art_mc(const ArtArgs& a, char* ws, int groups, hipStream_t st) {
+hipError_t launch_art_mc(const ArtArgs& a, char* ws, int groups, int late, hipStream_t st) {
   const int units = a.B * a.Hkv;
-  art_ring_init<4 * GR, D, kArtRingSlots><<<units, 128, 0, st>>>(ws);
-  art_mc_kernel<T, D, GR, 7, kArtRingSlots><<<units * groups, 8 * 64, 0, st>>>(a, ws, groups);
+  art_ring_init<4 * GR, D, kArtRingSlots><<<units, 128, 0, st>>>(ws, a.blocks_fetched);
+  art_mc_kernel<T, D, GR, 7, kArtRingSlots><<<units * groups + late, 8 * 64, 0, st>>>(a, ws, groups);
   return hipGetLastError();
 }
 
@@ -862,8 +986,12 @@ hipError_t launch_art_t(const ArtArgs& a, void* ws, size_t ws_bytes, hipStream_t
   if (e != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   if (ws && units <= kArtMcMaxUnits && 2 * units <= cus && ws_bytes >= (size_t)units * art_ring_bytes<D>(G)) {
+    // one workgroup per CU at the start, then as many again that join the
+    // units still running as CUs free up
     const int groups = min(kArtMcMaxGroups, cus / units);
-    return G > 4 ? launch_art_mc<T, D, 2>(a, (char*)ws, groups, st) : launch_art_mc<T, D, 1>(a, (char*)ws, groups, st);
+    const int late = units * groups;
+    return G > 4 ? launch_art_mc<T, D, 2>(a, (char*)ws, groups, late, st)
+                 : launch_art_mc<T, D, 1>(a, (char*)ws, groups, late, st);
   }
   const dim3 grid(units);
   const bool wide = units >= cus;
