@@ -146,12 +146,17 @@ int routed_run(const attn_dims* dims, int32_t n_layers, const uint8_t* route_mas
   for (int32_t i = 0; i < n_layers; ++i) {
     hipError_t e;
     if (route_mask[i]) {
-      // full attention: shard-aligned splits, merged per shard, then across shards
+      // full attention: shard-aligned splits, merged per shard, then across
+      // shards (both levels in one launch when a row's states fit one wave)
       skv::DecodeArgs a = decode_args(dims, q[i], k[i], v[i], seq_lens, S, m, l, o);
       e = skv::launch_decode(a, false, s);
-      if (e == hipSuccess)
+      if (e == hipSuccess && S <= 64) {
+        e = skv::launch_merge2(rows, n_shards, splits_per_shard, dims->head_dim, m, l, o, out[i], s);
+      } else if (e == hipSuccess) {
         e = skv::launch_merge(rows * n_shards, splits_per_shard, dims->head_dim, m, l, o, so, sm, sl, s);
-      if (e == hipSuccess) e = skv::launch_merge(rows, n_shards, dims->head_dim, sm, sl, so, out[i], nullptr, nullptr, s);
+        if (e == hipSuccess)
+          e = skv::launch_merge(rows, n_shards, dims->head_dim, sm, sl, so, out[i], nullptr, nullptr, s);
+      }
     } else {
       skv::DecodeArgs a = decode_args(dims, q[i], k[i], v[i], seq_lens, sa_splits, m, l, o);
       a.block_idx = sa_block_idx;

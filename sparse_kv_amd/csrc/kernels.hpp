@@ -50,6 +50,10 @@ struct ArtArgs {
 hipError_t launch_decode(const DecodeArgs& a, bool sparse, hipStream_t st);
 hipError_t launch_merge(int32_t rows, int32_t S, int32_t d, const float* m, const float* l,
                         const float* o, float* out, float* m_out, float* l_out, hipStream_t st);
+// Both levels of a shard merge in one launch (shards * inner <= 64): states
+// [rows, shards, inner] merged per shard, then across shards.
+hipError_t launch_merge2(int32_t rows, int32_t shards, int32_t inner, int32_t d, const float* m, const float* l,
+                         const float* o, float* out, hipStream_t st);
 // Paged K for the centroid kernels: null table = contiguous k.
 struct PagedK {
   const int32_t* table;

@@ -116,7 +116,86 @@ __global__ __launch_bounds__(256) void merge_kernel(int32_t rows, int32_t S, con
   }
 }
 
+// Two-level merge in one launch: the S = shards * inner states of a row are
+// merged per shard (inner consecutive states) into shard states (M_k, L_k,
+// O_k), and those across shards into the output: with w_s = l_s e^(m_s - M_k)
+// and W_k = L_k e^(M_k - M), out = sum_k W_k O_k / sum_k W_k and
+// O_k = sum_{s in k} w_s o_s / L_k, i.e. out = sum_s (W_k / L_k) w_s o_s /
+// sum_k W_k -- the merge of the inner states followed by the merge of the
+// shard states, as one weighted sum.  One wave per row, S <= 64: lane s holds
+// state s, and every split output is loaded in one round trip.
+template <int D>
+__global__ __launch_bounds__(256) void merge2_kernel(int32_t rows, int32_t shards, int32_t inner,
+                                                     const float* __restrict__ m, const float* __restrict__ l,
+                                                     const float* __restrict__ o, float* __restrict__ out) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int S = shards * inner;
+  const float* orow = o + (size_t)row * S * D + lane * PER;
+  // every split output, in flight with the states
+  float y[64][PER];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    if (i < S) {
+      load_row_part<PER>(orow + (size_t)i * D, y[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) y[i][e] = 0.f;
+    }
+  }
+  const float ms = lane < S ? m[(size_t)row * S + lane] : -INFINITY;
+  const float ls = lane < S ? l[(size_t)row * S + lane] : 0.f;
+  const int my_shard = lane / inner;
+  // first level: shard k's (M_k, L_k) into lane k; w_s into lane s
+  float Mk = -INFINITY, Lk = 0.f, wt = 0.f;
+  for (int k = 0; k < shards; ++k) {
+    const bool mine = lane < S && my_shard == k && ls > 0.f;
+    const float M = wave_max(mine ? ms : -INFINITY);
+    const float w = mine ? ls * fast_exp2((ms - M) * kLog2e) : 0.f;
+    if (my_shard == k) wt = w;
+    const float L = wave_sum(w);
+    if (lane == k) {
+      Mk = L > 0.f ? M : -INFINITY;
+      Lk = L;
+    }
+  }
+  // second level: the shard weights W_k, and each split's coefficient
+  const float Mall = wave_max(Lk > 0.f ? Mk : -INFINITY);
+  const float Wk = Lk > 0.f ? Lk * fast_exp2((Mk - Mall) * kLog2e) : 0.f;
+  const float Wsum = wave_sum(Wk);
+  const int src = min(my_shard, 63);
+  const float Ws = __shfl(Wk, src), Ls = __shfl(Lk, src);
+  const float coef = (wt > 0.f && Ls > 0.f) ? wt * (Ws / Ls) : 0.f;
+  float res[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) res[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    if (i < S) {
+      const float f = readlane(coef, i);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) res[e] = f != 0.f ? fmaf(f, y[i][e], res[e]) : res[e];
+    }
+  }
+  float* dst = out + (size_t)row * D + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) dst[e] = Wsum > 0.f ? res[e] / Wsum : 0.f;
+}
+
 }  // namespace
+
+hipError_t launch_merge2(int32_t rows, int32_t shards, int32_t inner, int32_t d, const float* m, const float* l,
+                         const float* o, float* out, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((rows + 3) / 4);
+  if (d == 128)
+    merge2_kernel<128><<<grid, 256, 0, st>>>(rows, shards, inner, m, l, o, out);
+  else
+    merge2_kernel<64><<<grid, 256, 0, st>>>(rows, shards, inner, m, l, o, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(int32_t rows, int32_t S, int32_t d, const float* m, const float* l,
                         const float* o, float* out, float* m_out, float* l_out, hipStream_t st) {

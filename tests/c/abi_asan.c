@@ -110,8 +110,9 @@ int main(void) {
     free(ws);
   }
 
-  /* the routed stack: 3 launches per full layer, 2 per sink + window layer, every
-     state pointer inside the workspace */
+  /* the routed stack: 2 launches per layer (decode, then both merge levels or the split
+     merge), every state pointer inside the workspace; 3 per full layer when a row's
+     shard-by-split states exceed one wave (9 shards x 8 splits) */
   {
     const uint8_t mask[3] = {1, 0, 1};
     const void* ptrs[3] = {fake, fake, fake};
@@ -122,8 +123,18 @@ int main(void) {
     stub_reset();
     CHECK(attn_decode_routed(&d, 3, mask, ptrs, ptrs, ptrs, NULL, 8, 2, fi, fi, 4, 4, ws, need, outs, NULL) ==
           ATTN_OK);
-    CHECK(stub_launches == 8);
+    CHECK(stub_launches == 6);
     for (i = 0; i < 3; ++i) CHECK(inside(stub_last_ptr[i], ws, need));
+    {
+      const size_t need72 = attn_routed_workspace_bytes(&d, 9, 8, 4);
+      char* ws72 = (char*)malloc(need72);
+      stub_reset();
+      CHECK(attn_decode_routed(&d, 3, mask, ptrs, ptrs, ptrs, NULL, 9, 8, fi, fi, 4, 4, ws72, need72, outs, NULL) ==
+            ATTN_OK);
+      CHECK(stub_launches == 8);
+      for (i = 0; i < 3; ++i) CHECK(inside(stub_last_ptr[i], ws72, need72));
+      free(ws72);
+    }
     CHECK(attn_decode_routed(&d, 3, mask, ptrs, ptrs, ptrs, NULL, 8, 2, fi, fi, 4, 4, ws, need - 1, outs, NULL) ==
           ATTN_ERR_WORKSPACE);
     free(ws);
@@ -135,7 +146,7 @@ int main(void) {
       stub_reset();
       CHECK(attn_decode_routed_static(&d, 3, mask, ptrs, ptrs, ptrs, NULL, 8, 2, fi, fi, 4, 4, outs, NULL) ==
             ATTN_OK);
-      CHECK(stub_launches == 8);
+      CHECK(stub_launches == 6);
       for (i = 0; i < 3; ++i) {
         first[i] = stub_last_ptr[i];
         CHECK(first[i] != NULL && ((uintptr_t)first[i] & 255) == 0);

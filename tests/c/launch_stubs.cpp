@@ -59,6 +59,16 @@ hipError_t launch_merge(int32_t rows, int32_t, int32_t, const float* m, const fl
   stub_last_S = rows;
   return hipSuccess;
 }
+hipError_t launch_merge2(int32_t rows, int32_t, int32_t, int32_t, const float* m, const float* l, const float* o,
+                         float* out, hipStream_t) {
+  ++stub_launches;
+  stub_last_ptr[0] = m;
+  stub_last_ptr[1] = l;
+  stub_last_ptr[2] = o;
+  stub_last_ptr[3] = out;
+  stub_last_S = rows;
+  return hipSuccess;
+}
 hipError_t launch_build_centroids(const void*, const int32_t*, float*, int32_t, int32_t, int32_t, int32_t, int32_t,
                                   hipStream_t, PagedK) {
   ++stub_launches;

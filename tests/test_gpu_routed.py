@@ -16,6 +16,7 @@ pytestmark = pytest.mark.gpu
     ([1, 1, 1], 1, 1, 1),              # every layer full, one shard of one split
     ([0, 0, 0], 3, 5, 7),              # every layer sink + window
     ([0, 1, 1, 0], 8, 4, 32),          # the benchmark's split counts
+    ([1, 0, 1], 9, 8, 5),              # 72 states per row: the two merge levels as separate launches
 ])
 def test_routed_stack_matches_oracle(mask, n_shards, sps, sa_splits):
     log(f"[routed] {len(mask)}-layer stack {mask}, {n_shards} shards x {sps} splits, {sa_splits} SA splits; "
