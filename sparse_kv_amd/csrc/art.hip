@@ -16,8 +16,9 @@
 //     else 16).
 //   * 1 folder wave folds the published states strictly in visit order into
 //     the running state -- the result of a one-block-at-a-time streaming
-//     kernel -- a batch of consecutive published positions at a time, and
-//     evaluates the stop rule per query head at every position of the batch.
+//     kernel -- a batch of whole groups of consecutive published positions at
+//     a time, and evaluates the stop rule per query head at every position of
+//     the batch.
 //     A head that stops freezes its state; when every head of the group has
 //     stopped (or the positions run out) the folder writes the outputs.
 // Visit positions come from the default order, an explicit order, or a
@@ -35,9 +36,9 @@
 // to a caller-provided workspace in device memory (128 slots, device-scope
 // accesses), producers claim visit positions from a per-unit counter, and
 // four folder waves (one per query head, or per two heads when G > 4) fold
-// batches of up to 64 (32) positions; with one head per wave a batch's
-// running states come from wave-wide DPP prefix sums against one reference
-// max.
+// batches of up to 64 (32) positions.  Folders take whole aligned groups of
+// positions and carry the running state from group to group, so every
+// result is bitwise reproducible whatever the timing of the producers.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -68,7 +69,7 @@ struct ArtWaves {
   static constexpr int kScratch = kKRows ? 64 * kKStride : 64 * GP * 4;
   __attribute__((aligned(16))) char scratch[NP][kScratch];
   float fold_w[kMaxFolders][64];  // per folder: (head, batch position) output weights
-  float fold_a[kMaxFolders][GP];  // per folder: per head rescale of the running output
+  float fold_a[kMaxFolders][16];  // per folder: per (head, group) rescale of the running output
 };
 
 // The ring through which producers hand block states (m, l, unnormalised
@@ -536,59 +537,28 @@ __device__ __forceinline__ float shr(float x) {
     return __shfl(x, ((int)threadIdx.x - K) & 63);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave, all in DPP: row_shr 1, 2,
-// 4, 8 within rows of 16 (lanes whose source lies in the previous row add 0),
-// then row_bcast:15 adds row 0's total to row 1 and row 2's to row 3, and
-// row_bcast:31 adds the first 32 lanes' total to rows 2 and 3.
-__device__ __forceinline__ float wave_prefix_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
-  return x;
-}
-
-// One inclusive-scan step over groups of CH lanes: lanes at group position
-// j >= K take the state of lane j - K as the earlier part.
-template <int K, int CH, int PW>
-__device__ __forceinline__ void scan_step(int j, float& m, float& l, float (&a)[PW]) {
-  if constexpr (K < CH) {
-    const float me = shr<K, CH>(m), le = shr<K, CH>(l);
+// One step of an inclusive online-softmax scan within aligned groups of GS
+// lanes (GS <= 16, so a group never crosses a row of 16 lanes): the lane at
+// group offset o >= K merges in the state of lane - K.
+template <int K, int GS, int PW>
+__device__ __forceinline__ void group_scan_step(int j, float& m, float& l, float (&a)[PW]) {
+  if constexpr (K < GS) {
+    const float me = shr<K, 16>(m), le = shr<K, 16>(l);
     float ae[PW];
 #pragma unroll
-    for (int k = 0; k < PW; ++k) ae[k] = shr<K, CH>(a[k]);
-    if (j >= K) merge_into<PW>(me, le, ae, m, l, a);
+    for (int k = 0; k < PW; ++k) ae[k] = shr<K, 16>(a[k]);
+    if (j % GS >= K) merge_into<PW>(me, le, ae, m, l, a);
   }
 }
 
-// One inclusive prefix-sum step over groups of CH lanes.
-template <int K, int CH, int PW>
-__device__ __forceinline__ void sum_step(int j, float& l, float (&a)[PW]) {
-  if constexpr (K < CH) {
-    const float le = shr<K, CH>(l);
-    float ae[PW];
-#pragma unroll
-    for (int k = 0; k < PW; ++k) ae[k] = shr<K, CH>(a[k]);
-    if (j >= K) {
-      l += le;
-#pragma unroll
-      for (int k = 0; k < PW; ++k) a[k] += ae[k];
-    }
-  }
-}
-
-// Maximum over each group of CH consecutive lanes (8, 16, 32 or 64), in every lane.
+// The value of lane src, for a src that is the same across each head's CH
+// lanes (wave-uniform when one head fills the wave).
 template <int CH>
-__device__ __forceinline__ float group_max(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror: groups of 8
-  if constexpr (CH >= 16) x = fmaxf(x, dpp<0x140>(x));  // row_mirror: groups of 16
-  if constexpr (CH >= 32) x = xrow16_max(x);
-  if constexpr (CH >= 64) x = xhalf_max(x);
-  return x;
+__device__ __forceinline__ float from_lane(float x, int src) {
+  if constexpr (CH == 64)
+    return readlane(x, __builtin_amdgcn_readfirstlane(src));
+  else
+    return __shfl(x, src);
 }
 
 // Probe of a state: norm n and unit direction u of the first P channels of
@@ -610,33 +580,42 @@ __device__ __forceinline__ void probe_of(float L, const float (&A)[PW], float& n
 
 // A folder wave.  It folds published block states strictly in visit order,
 // as a one-block-at-a-time streaming kernel would, but a batch at a time:
-// every consecutive position already published (up to CH = 64 / HPW, and
-// the ring's batch cap) is taken at once.  Folder f owns heads
-// f * HPW .. f * HPW + HPW - 1.  In the scan layout lane (h, j) = h * CH + j
-// holds head h's state of the batch's block j; an inclusive scan over j
-// (DPP row shifts, lane permutes past 16) gives the running state after
-// every block of the batch, from which each lane evaluates the stop rule
-// for its position.  Consecutive-stable runs come from the ballot of the
-// per-position decisions, so one batch costs about as much as one block
-// did.  A head that stops keeps its state at its stop position.  The full
-// output (all d channels) only needs the state at the end of each batch (or
-// at the stop): lane (h, j) folds channels j * D / CH .. of head h with
-// per-block weights exp2(m_j - M), staged in LDS.  PW probe channels are
-// carried (probe_dim <= PW).
+// every whole aligned group of GS consecutive positions already published
+// (up to CH = 64 / HPW positions and the ring's batch cap; the sequence's
+// last group may be short) is taken at once.  Folder f owns heads
+// f * HPW .. f * HPW + HPW - 1; in the scan layout lane (h, j) = h * CH + j
+// holds head h's state of the batch's block j.  Every running state is
+// computed the same way whatever the batch boundaries, so results are
+// bitwise reproducible however the producers' timing falls: an online-
+// softmax scan within each group gives the group's prefix states, the state
+// before each group follows from the one before the batch by merging in the
+// groups' totals one group after another, and each position's running state
+// is that carry merged with its prefix.  Each lane then evaluates the stop
+// rule for its position; consecutive-stable runs come from the ballot of the
+// per-position decisions.  A head that stops keeps its state at its stop
+// position.  The full output (all d channels) is folded group by group: lane
+// (h, j) holds channels j * D / CH .. of head h, rescales them to each
+// group's closing max and adds the group's blocks with weights
+// exp2(m_i - M), staged in LDS.  PW probe channels are carried
+// (probe_dim <= PW).
 template <typename T, int D, int HPW, int PW, typename SH, typename RING>
 __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int f, int b, int g, int G, int nv) {
   constexpr int CH = 64 / HPW;  // batch positions per head; lanes per head
+  // positions per group: few groups per batch keep the serial carry chain
+  // short; small groups keep the folder from waiting on a straggling block
+  constexpr int GS = CH >= 64 ? 16 : (CH >= 32 ? 8 : 4);
   constexpr int kR = RING::kR;
   constexpr int NBT = CH < RING::kMaxBatch ? CH : RING::kMaxBatch;  // largest batch
   constexpr int FE = D / CH;    // output channels per lane
   constexpr uint64_t RM = CH == 64 ? ~0ull : ((1ull << CH) - 1ull);
   static_assert(PW % 4 == 0 && PW <= 16 && FE >= 1, "layout");
+  static_assert(NBT % GS == 0 && kR % GS == 0, "whole groups per batch and ring");
   const int lane = threadIdx.x & 63;
   const int hh = lane / CH, j = lane % CH;  // scan and output layout
   const int head = f * HPW + hh;            // head of the unit
   const int P = p.probe_dim;
   float* fold_w = sh.fold_w[f];
-  float* fold_a = sh.fold_a[f];
+  float* fold_a = sh.fold_a[f];  // per (head, group): rescale of the output before the group
 
   // running state of head hh, identical in the CH lanes of its group
   float cM = -INFINITY, cL = 0.f, cA[PW];
@@ -651,11 +630,13 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int f, int b, i
   int t0 = 0;
   // a folder with no real head (padded groups) takes no part
   while (__ballot(live) != 0 && t0 < nv) {
-    // length of the published run of positions t0, t0 + 1, ...
+    // length of the published run of positions t0, t0 + 1, ..., cut to
+    // whole groups short of the sequence's end
     const int tj = t0 + j;
     const bool pub = j < NBT && tj < nv && ring.poll(tj % kR) == tj;
     const uint64_t pm = (uint64_t)__ballot(pub) & RM;  // group 0 checks every position
-    const int n = ~pm == 0 ? 64 : __builtin_ctzll(~pm);
+    int n = ~pm == 0 ? 64 : __builtin_ctzll(~pm);
+    if (t0 + n < nv) n -= n % GS;
     if (n == 0) {
       __builtin_amdgcn_s_sleep(1);
       continue;
@@ -677,47 +658,42 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int f, int b, i
       }
     }
     const float mb = m;
-    // The running state after every block of the batch.  Usually all of them
-    // are taken relative to one reference, the largest block max of the batch
-    // and the carry: each block's (l, a) scaled by exp2(m_j - Mref), then
-    // plain prefix sums.  That holds whenever the first running max is within
-    // 2^100 of Mref (so no running sum can underflow); otherwise the batch
-    // takes the online-softmax merge at every scan step.
-    const float Mref = fmaxf(group_max<CH>(mb), cM);
-    const float Mrs = Mref == -INFINITY ? 0.f : Mref;
-    const float first = fmaxf(cM, CH == 64 ? readlane(mb, 0) : __shfl(mb, hh * CH));
-    if (__ballot(!(first >= Mrs - 100.f) && live) == 0) {
-      const float wj = in ? fast_exp2(mb - Mrs) : 0.f;
-      l *= wj;
+    // prefix states within each group
+    group_scan_step<1, GS, PW>(j, m, l, a);
+    group_scan_step<2, GS, PW>(j, m, l, a);
+    group_scan_step<4, GS, PW>(j, m, l, a);
+    group_scan_step<8, GS, PW>(j, m, l, a);
+    // the state before each group, group after group from the state before
+    // the batch, into (gM, gL, gA) of the lanes of that group
+    float gM = cM, gL = cL, gA[PW];
 #pragma unroll
-      for (int k = 0; k < PW; ++k) a[k] *= wj;
-      if constexpr (CH == 64) {
-        l = wave_prefix_sum(l);
+    for (int k = 0; k < PW; ++k) gA[k] = cA[k];
+    {
+      float xM = cM, xL = cL, xA[PW];
 #pragma unroll
-        for (int k = 0; k < PW; ++k) a[k] = wave_prefix_sum(a[k]);
-      } else {
-        sum_step<1, CH, PW>(j, l, a);
-        sum_step<2, CH, PW>(j, l, a);
-        sum_step<4, CH, PW>(j, l, a);
-        sum_step<8, CH, PW>(j, l, a);
-        sum_step<16, CH, PW>(j, l, a);
-        sum_step<32, CH, PW>(j, l, a);
+      for (int k = 0; k < PW; ++k) xA[k] = cA[k];
+      const int ng = (n + GS - 1) / GS;
+      for (int q = 1; q < ng; ++q) {
+        const int src = hh * CH + q * GS - 1;  // the previous group's last block (groups before the last are whole)
+        float tM = from_lane<CH>(m, src), tL = from_lane<CH>(l, src);
+        float tA[PW];
+#pragma unroll
+        for (int k = 0; k < PW; ++k) tA[k] = from_lane<CH>(a[k], src);
+        merge_into<PW>(xM, xL, xA, tM, tL, tA);
+        xM = tM;
+        xL = tL;
+#pragma unroll
+        for (int k = 0; k < PW; ++k) xA[k] = tA[k];
+        if (j / GS == q) {
+          gM = xM;
+          gL = xL;
+#pragma unroll
+          for (int k = 0; k < PW; ++k) gA[k] = xA[k];
+        }
       }
-      const float cw = cL > 0.f ? fast_exp2(cM - Mrs) : 0.f;
-      l = fmaf(cw, cL, l);
-#pragma unroll
-      for (int k = 0; k < PW; ++k) a[k] = fmaf(cw, cA[k], a[k]);
-      m = Mref;
-    } else {
-      scan_step<1, CH, PW>(j, m, l, a);
-      scan_step<2, CH, PW>(j, m, l, a);
-      scan_step<4, CH, PW>(j, m, l, a);
-      scan_step<8, CH, PW>(j, m, l, a);
-      scan_step<16, CH, PW>(j, m, l, a);
-      scan_step<32, CH, PW>(j, m, l, a);
-      // state after block j = carry (+) scan_j
-      merge_into<PW>(cM, cL, cA, m, l, a);
     }
+    // running state after block j = carry of its group (+) its group prefix
+    merge_into<PW>(gM, gL, gA, m, l, a);
     float nrm, u[PW];
     probe_of<PW>(l, a, nrm, u);
     float cn, cu[PW];
@@ -747,43 +723,40 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int f, int b, i
     const bool hit = st && run >= p.patience;
     const uint64_t rowh = ((uint64_t)__ballot(hit) >> (hh * CH)) & RM;
     const int jend = rowh ? __builtin_ctzll(rowh) : n - 1;
-    // the new running state: the state at jend (one lane for the whole wave
-    // when a wave folds one head)
-    float nM, nL, nA[PW];
-    int nrun;
-    if constexpr (CH == 64) {
-      const int src = __builtin_amdgcn_readfirstlane(jend);
-      nM = readlane(m, src);
-      nL = readlane(l, src);
-      nrun = __builtin_amdgcn_readlane(run, src);
+    // the new running state: the state at jend
+    const int src = hh * CH + jend;
+    const float nM = from_lane<CH>(m, src), nL = from_lane<CH>(l, src);
+    const int nrun = CH == 64 ? __builtin_amdgcn_readlane(run, __builtin_amdgcn_readfirstlane(src)) : __shfl(run, src);
+    float nA[PW];
 #pragma unroll
-      for (int k = 0; k < PW; ++k) nA[k] = k < P ? readlane(a[k], src) : 0.f;
-    } else {
-      const int src = hh * CH + jend;
-      nM = __shfl(m, src);
-      nL = __shfl(l, src);
-      nrun = __shfl(run, src);
-#pragma unroll
-      for (int k = 0; k < PW; ++k) nA[k] = k < P ? __shfl(a[k], src) : 0.f;
-    }
-    // weights of the batch's blocks in the new state, staged for the output fold
-    const float nMs = nM == -INFINITY ? 0.f : nM;
-    fold_w[lane] = (in && j <= jend) ? fast_exp2(mb - nMs) : 0.f;
-    if (j == 0) fold_a[hh] = live ? fast_exp2(cM - nMs) : 1.f;
+    for (int k = 0; k < PW; ++k) nA[k] = k < P ? from_lane<CH>(a[k], src) : 0.f;
+    // output fold weights: each block of a group up to jend relative to the
+    // running max where the group closes (its last block, or jend), and per
+    // group the rescale of the output from the max before the group
+    const int gq = j / GS;
+    const int gend = min(gq * GS + GS - 1, jend);
+    const float Me = __shfl(m, hh * CH + gend);  // per lane: its group's closing max
+    const float Mes = Me == -INFINITY ? 0.f : Me;
+    fold_w[lane] = (in && j <= jend) ? fast_exp2(mb - Mes) : 0.f;
+    if (j % GS == 0 && j < NBT) fold_a[hh * (CH / GS) + gq] = (live && j <= jend) ? fast_exp2(gM - Mes) : 1.f;
     wave_lds_exchange();  // the weights are read by the other lanes
     {
-      const float al = fold_a[hh];
-#pragma unroll
-      for (int e = 0; e < FE; ++e) A[e] *= al;
       // chunks of positions whose rows are all loaded before any is used;
       // positions past the batch reread its last slot with weight 0
-      constexpr int CK = (64 / FE < 32 ? 64 / FE : 32) < NBT ? (64 / FE < 32 ? 64 / FE : 32) : NBT;
+      constexpr int CK0 = (64 / FE < 32 ? 64 / FE : 32) < NBT ? (64 / FE < 32 ? 64 / FE : 32) : NBT;
+      constexpr int CK = CK0 < GS ? GS : CK0;
+      static_assert(CK % GS == 0, "chunks of whole groups");
       for (int j0 = 0; j0 < n; j0 += CK) {
         float x[CK][FE];
 #pragma unroll
         for (int jj = 0; jj < CK; ++jj) ring.acc_row((t0 + min(j0 + jj, n - 1)) % kR, head, j * FE, x[jj]);
 #pragma unroll
         for (int jj = 0; jj < CK; ++jj) {
+          if (jj % GS == 0 && j0 + jj < n) {
+            const float al = fold_a[hh * (CH / GS) + (j0 + jj) / GS];
+#pragma unroll
+            for (int e = 0; e < FE; ++e) A[e] *= al;
+          }
           const float w = j0 + jj < n ? fold_w[hh * CH + j0 + jj] : 0.f;
 #pragma unroll
           for (int e = 0; e < FE; ++e) A[e] = fmaf(w, x[jj][e], A[e]);
