@@ -769,12 +769,47 @@ def run_ceiling(reps=10):
                 if rc != 0:
                     raise RuntimeError(f"skv_bench_stream_read failed ({rc})")
         sweep[wgs] = nbytes / (t.median_ms() * 1e-3) / 1e9
-    del buf, sink
+    del buf
     torch.cuda.empty_cache()
     best = max(sweep, key=sweep.get)
     return dict(kernel="stream_read_kernel (non-temporal 16-byte loads, whole lines)", bytes=nbytes,
                 gbs=sweep[best], pct_peak=100 * sweep[best] / PEAK_HBM_GBS, workgroups=best,
-                sweep_gbs={str(k_): round(v_, 1) for k_, v_ in sweep.items()})
+                sweep_gbs={str(k_): round(v_, 1) for k_, v_ in sweep.items()},
+                launch_us=run_launch_floor(lib, sink))
+
+
+def run_launch_floor(lib, sink, launches=200, reps=10):
+    """Fixed cost per kernel launch: a chain of empty 256-workgroup launches captured in a HIP graph,
+    replayed and timed with events; the median time per launch, in microseconds."""
+    import ctypes
+
+    import torch
+
+    f = lib.skv_bench_empty
+    f.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+
+    def chain():
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _ in range(launches):
+            if f(256, ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+                raise RuntimeError("skv_bench_empty failed")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain()
+    t = _timer()
+    for i in range(reps + 2):
+        with (t if i >= 2 else _timer()):
+            g.replay()
+    del g
+    return t.median_ms() * 1e3 / launches
 
 
 def cpu_baseline(inp, budget_s, topk, n_sink, n_recent, win_recent, tau, phi, patience, probe, bytes_per_unit):

@@ -1,7 +1,8 @@
 /*
- * Measurement helper of the benchmark (libsparse_kv_bench.so), not part of
+ * Measurement helpers of the benchmark (libsparse_kv_bench.so), not part of
  * the decode-attention interface: a streaming-read kernel whose rate is the
- * achievable HBM read ceiling the decode kernels are compared with.
+ * achievable HBM read ceiling the decode kernels are compared with, and an
+ * empty kernel whose launches give the fixed cost of one launch.
  */
 #ifndef SPARSE_KV_BENCH_H
 #define SPARSE_KV_BENCH_H
@@ -26,6 +27,15 @@ extern "C" {
  * Queued on `stream` (a hipStream_t); nothing is allocated.
  */
 int skv_bench_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
+
+/*
+ * Queue one launch of a kernel that does no work, with `workgroups`
+ * workgroups of 256 threads, on `stream`.  A chain of these, timed as a
+ * captured graph, gives the fixed cost per launch.
+ *   sink  device uint32 [workgroups * 256]; never written.
+ * Returns 0, -1 on invalid arguments, -3 when the launch fails.
+ */
+int skv_bench_empty(int32_t workgroups, uint32_t* sink, void* stream);
 
 #pragma GCC visibility pop
 

@@ -1,6 +1,7 @@
-// Streaming-read probe for the benchmark: the achievable HBM read rate of
-// this device, the ceiling the decode kernels are compared with beside the
-// datasheet peak.  Not part of the decode library (its own shared object).
+// Probes for the benchmark: the achievable HBM read rate of this device, the
+// ceiling the decode kernels are compared with beside the datasheet peak, and
+// the fixed cost of one kernel launch.  Not part of the decode library (its
+// own shared object).
 //
 // Every workgroup streams one contiguous slice of the buffer with
 // non-temporal 16-byte buffer loads, each wave-wide load covering 1 KiB (8
@@ -50,7 +51,22 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* buf, 
   if (acc == 0x9E3779B9u) sink[blockIdx.x * kThreads + threadIdx.x] = acc;
 }
 
+// A kernel that does no work: a dependent chain of these on one stream
+// (captured in a HIP graph, so the host is out of the way) takes, per launch,
+// the fixed cost every kernel carries -- dispatch, the workgroups' start and
+// end, the completion that the next launch waits for.  That is the floor
+// under a stage made of several short launches.
+__global__ __launch_bounds__(kThreads) void empty_kernel(uint32_t* sink, uint32_t never) {
+  if (never == 0x9E3779B9u) sink[blockIdx.x * kThreads + threadIdx.x] = never;
+}
+
 }  // namespace
+
+extern "C" int skv_bench_empty(int32_t workgroups, uint32_t* sink, void* stream) {
+  if (!sink || workgroups < 1) return -1;
+  empty_kernel<<<workgroups, kThreads, 0, (hipStream_t)stream>>>(sink, 0u);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 extern "C" int skv_bench_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
                                      void* stream) {

@@ -162,15 +162,24 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in DPP: row_shr 1, 2, 4,
+// 8 within rows of 16 (a lane whose source lies in the previous row adds 0),
+// then row_bcast:15 adds row 0's total to row 1 and row 2's to row 3, and
+// row_bcast:31 adds the first 32 lanes' total to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+  return x;
+}
+
 // Exclusive prefix sum of one int per thread over a 256-thread workgroup.
 __device__ int block_exscan(int x, int* total, int* lds4) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int inc = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off);
-    if (lane >= off) inc += y;
-  }
+  const int inc = wave_incl_sum(x);
   if (lane == 63) lds4[w] = inc;
   __syncthreads();
   int base = 0, tot = 0;
@@ -190,15 +199,7 @@ __device__ int block_exscan(int x, int* total, int* lds4) {
 __device__ int block_exscan2(int a, int b, int* tot_a, int* tot_b, int* pre_b) {
   __shared__ int lds[2][4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int ia = a, ib = b;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int ya = __shfl_up(ia, off), yb = __shfl_up(ib, off);
-    if (lane >= off) {
-      ia += ya;
-      ib += yb;
-    }
-  }
+  const int ia = wave_incl_sum(a), ib = wave_incl_sum(b);
   if (lane == 63) {
     lds[0][w] = ia;
     lds[1][w] = ib;
@@ -262,13 +263,16 @@ __device__ void radix_select(int n, int kk, KeyF key, EligF elig, uint32_t* hist
 // bin holding it (thread t sums bins 4095 - 16t ...; one block scan), then
 // that bin's keys are ranked against each other.  False -- nothing decided
 // -- when that bin holds more than 256 keys (heavy ties or clustering).
+// `cleared`: the histogram is already zero and that is visible to every thread.
 template <typename KeyF, typename EligF>
 __device__ bool select_wide(int n, int kk, KeyF key, EligF elig, uint32_t* hist, uint32_t* cand, int* scan4,
-                            uint32_t* sh_prefix, int* sh_rem, uint32_t& thr, int& need_eq) {
+                            uint32_t* sh_prefix, int* sh_rem, uint32_t& thr, int& need_eq, bool cleared) {
   __shared__ int sh[4];
   const int tid = threadIdx.x;
-  for (int i = tid; i < 4096; i += 256) hist[i] = 0;
-  __syncthreads();
+  if (!cleared) {
+    for (int i = tid; i < 4096; i += 256) hist[i] = 0;
+    __syncthreads();
+  }
   for (int i = tid; i < n; i += 256)
     if (elig(i)) atomicAdd(&hist[key(i) >> 20], 1u);
   __syncthreads();
@@ -323,10 +327,11 @@ __device__ bool select_wide(int n, int kk, KeyF key, EligF elig, uint32_t* hist,
 // Each thread owns a contiguous chunk, so ranks follow the index order.
 // Returns the number taken.
 // With WIDE, hist holds 4096 entries and cand 256, and the threshold comes
-// from select_wide when it can decide.  ALL: every item is eligible.
+// from select_wide when it can decide (`cleared`: hist is already zero).
+// ALL: every item is eligible.
 template <bool WIDE = false, bool ALL = false, typename KeyF, typename EligF, typename TakeF>
 __device__ int take_best(int n, int kk, KeyF key, EligF elig, TakeF take, uint32_t* hist, int* scan4,
-                         uint32_t* sh_prefix, int* sh_rem, uint32_t* cand = nullptr) {
+                         uint32_t* sh_prefix, int* sh_rem, uint32_t* cand = nullptr, bool cleared = false) {
   const int tid = threadIdx.x;
   const int CH = (n + 255) / 256;
   const int i0 = min(tid * CH, n), i1 = min(i0 + CH, n);
@@ -342,7 +347,8 @@ __device__ int take_best(int n, int kk, KeyF key, EligF elig, TakeF take, uint32
   int need_eq = 0;
   if (ranked) {
     bool done = false;
-    if constexpr (WIDE) done = select_wide(n, kq, key, elig, hist, cand, scan4, sh_prefix, sh_rem, thr, need_eq);
+    if constexpr (WIDE)
+      done = select_wide(n, kq, key, elig, hist, cand, scan4, sh_prefix, sh_rem, thr, need_eq, cleared);
     if (!done) radix_select(n, kq, key, elig, hist, scan4, sh_prefix, sh_rem, thr, need_eq);
   }
   // per chunk: keys equal to the threshold and keys above it (every
@@ -381,7 +387,12 @@ __device__ int take_best(int n, int kk, KeyF key, EligF elig, TakeF take, uint32
 // The candidates' order-preserving keys are staged in LDS once (rows of up
 // to kTopkStage candidates; longer rows are read from memory in every pass),
 // then take_best's radix select and index-ordered compaction pick the k.
+// The staging requests kTopkPer scores per thread before storing any, and
+// the first of them together with the sequence length, so a row of up to
+// 256 * kTopkPer blocks costs one round trip to memory (one load at a time
+// was a round trip per 256 blocks, most of the kernel's time).
 constexpr int kTopkStage = 16384;
+constexpr int kTopkPer = 8;
 
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
                                                    int32_t Hkv, int32_t NBmax, int32_t k, int32_t n_sink,
@@ -394,18 +405,43 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   __shared__ uint32_t sh_prefix;
   __shared__ int sh_rem;
   const int unit = blockIdx.x, b = unit / Hkv, tid = threadIdx.x;
-  const int L = clampi(seq_lens ? seq_lens[b] : NBmax * kBlock, 0, NBmax * kBlock);
-  const int nb = (L + kBlock - 1) / kBlock;
   const float* row = scores + (size_t)unit * NBmax;
   int32_t* out = idx + (size_t)unit * max_sel;
+  const int Lraw = seq_lens ? seq_lens[b] : NBmax * kBlock;
+  // the row's first scores, requested before the length is known (with k = 0
+  // no score is read: scores may be null)
+  float x0[kTopkPer];
+#pragma unroll
+  for (int u = 0; u < kTopkPer; ++u) {
+    const int jb = u * 256 + tid;
+    x0[u] = (k > 0 && jb < NBmax) ? row[jb] : 0.f;
+  }
+  // the histogram's clear overlaps those loads
+  for (int i = tid; i < 4096; i += 256) hist[i] = 0;
+  const int L = clampi(Lraw, 0, NBmax * kBlock);
+  const int nb = (L + kBlock - 1) / kBlock;
 
   // forced blocks: [0, sink_hi) and [rec_lo, nb); candidates: [sink_hi, rec_lo)
   const int sink_hi = min(n_sink, nb);
   const int rec_lo = max(nb - n_recent, sink_hi);
   const int ncand = rec_lo - sink_hi;
   const bool staged = ncand <= kTopkStage;
-  if (staged && k > 0)  // with k = 0 no score is read (scores may be null)
-    for (int i = tid; i < ncand; i += 256) keys[i] = score_key(row[sink_hi + i]);
+  if (staged && k > 0) {
+    // blocks jb = base + u * 256 + tid of the row; candidates go to keys[jb - sink_hi]
+    for (int base = 0; base < rec_lo; base += 256 * kTopkPer) {
+      float x[kTopkPer];
+#pragma unroll
+      for (int u = 0; u < kTopkPer; ++u) {
+        const int jb = base + u * 256 + tid;
+        x[u] = base == 0 ? x0[u] : (jb < rec_lo ? row[jb] : 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kTopkPer; ++u) {
+        const int jb = base + u * 256 + tid;
+        if (jb >= sink_hi && jb < rec_lo) keys[jb - sink_hi] = score_key(x[u]);
+      }
+    }
+  }
   __syncthreads();
   auto key = [&](int i) { return staged ? keys[i] : score_key(row[sink_hi + i]); };
   auto put = [&](int i, int r) {
@@ -413,7 +449,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   };
   auto all = [](int) { return true; };
   // staged keys are cheap to read twice: one histogram pass usually decides
-  const int npick = staged ? take_best<true, true>(ncand, k, key, all, put, hist, scan4, &sh_prefix, &sh_rem, cand)
+  const int npick = staged ? take_best<true, true>(ncand, k, key, all, put, hist, scan4, &sh_prefix, &sh_rem, cand,
+                                                  true)
                            : take_best<false, true>(ncand, k, key, all, put, hist, scan4, &sh_prefix, &sh_rem);
   for (int j = tid; j < sink_hi; j += 256)
     if (j < max_sel) out[j] = j;

@@ -1,4 +1,4 @@
-"""The benchmark's streaming-read probe library loads, exports what
+"""The benchmark's probe library (streaming read, empty launch) loads, exports what
 include/sparse_kv_bench.h declares, and rejects bad arguments on the host
 (CPU only: no call here reaches a launch)."""
 
@@ -24,7 +24,12 @@ def blib():
 def test_exports_and_validation(blib):
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     names = set(re.findall(r"^\s*int\s+(skv_[a-z_]+)\s*\(", text, flags=re.M))
-    assert names == {"skv_bench_stream_read"}
+    assert names == {"skv_bench_stream_read", "skv_bench_empty"}
+    e = blib.skv_bench_empty
+    e.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    e.restype = ctypes.c_int
+    assert e(256, None, None) == -1
+    assert e(0, ctypes.c_void_p(0x1000), None) == -1
     f = blib.skv_bench_stream_read
     f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     f.restype = ctypes.c_int
