@@ -463,6 +463,171 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   if (tid == 0) n_sel[unit] = min(total, max_sel);
 }
 
+// Rows of at most kTopkSmall blocks (every row of a cache of up to 128K
+// tokens): thread t holds the keys of blocks t, t + 256, ... in registers
+// (round u = block / 256), so no phase reads keys back from LDS one load at
+// a time.  The k-th key comes from the 4096-bin histogram of the top 12 key
+// bits and the rank of the <= 256 keys in its bin, as in select_wide (an
+// 8-bit radix select over the keys staged in LDS when the bin holds more).
+// The chosen blocks are compacted in block order from per-round prefix
+// counts: block 256 u + t follows every block of rounds before u and the
+// blocks of round u held by lower threads.
+constexpr int kTopkSmall = 2048;
+constexpr int kSmallPer = kTopkSmall / 256;
+
+__global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict__ scores,
+                                                         const int32_t* __restrict__ seq_lens, int32_t Hkv,
+                                                         int32_t NBmax, int32_t k, int32_t n_sink, int32_t n_recent,
+                                                         int32_t max_sel, int32_t* __restrict__ idx,
+                                                         int32_t* __restrict__ n_sel) {
+  __shared__ uint32_t keys[kTopkSmall];  // the radix select's copy of the keys
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t cand[256];
+  __shared__ int scan4[4];
+  __shared__ int counts[2][kSmallPer][4];  // per round and wave: keys above, and equal to, the k-th key
+  __shared__ uint32_t sh_prefix;
+  __shared__ int sh_rem, sh_bin, sh_bin_rem, sh_bin_cnt, sh_cnt;
+  const int unit = blockIdx.x, b = unit / Hkv, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* row = scores + (size_t)unit * NBmax;
+  int32_t* out = idx + (size_t)unit * max_sel;
+  const int Lraw = seq_lens ? seq_lens[b] : NBmax * kBlock;
+  // every score of the row is requested before the length is known (with
+  // k = 0 no score is read: scores may be null)
+  float x[kSmallPer];
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) {
+    const int jb = u * 256 + tid;
+    x[u] = (k > 0 && jb < NBmax) ? row[jb] : 0.f;
+  }
+  for (int i = tid; i < 4096; i += 256) hist[i] = 0;
+  if (tid == 0) sh_cnt = 0;
+  const int L = clampi(Lraw, 0, NBmax * kBlock);
+  const int nb = (L + kBlock - 1) / kBlock;
+  // forced blocks: [0, sink_hi) and [rec_lo, nb); candidates: [sink_hi, rec_lo)
+  const int sink_hi = min(n_sink, nb);
+  const int rec_lo = max(nb - n_recent, sink_hi);
+  const int ncand = rec_lo - sink_hi;
+  const int kq = min(k, ncand);
+  const bool ranked = kq > 0 && kq < ncand;
+  uint32_t key[kSmallPer];
+  bool in[kSmallPer];
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) {
+    const int jb = u * 256 + tid;
+    in[u] = jb >= sink_hi && jb < rec_lo;
+    key[u] = in[u] ? score_key(x[u]) : 0u;
+  }
+  __syncthreads();  // the histogram is clear
+
+  // the k-th largest key (thr) and how many keys equal to it are taken
+  uint32_t thr = 0;
+  int need_eq = 0;
+  if (ranked) {
+#pragma unroll
+    for (int u = 0; u < kSmallPer; ++u)
+      if (in[u]) atomicAdd(&hist[key[u] >> 20], 1u);
+    __syncthreads();
+    int loc = 0;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) loc += (int)hist[4095 - 16 * tid - c];
+    int tot;
+    const int above = block_exscan(loc, &tot, scan4);  // keys in the bins above this thread's
+    if (above < kq && kq <= above + loc) {
+      int a = above;
+      for (int c = 0; c < 16; ++c) {
+        const int bin = 4095 - 16 * tid - c;
+        const int h = (int)hist[bin];
+        if (a + h >= kq) {
+          sh_bin = bin;
+          sh_bin_rem = kq - a;  // how many of the bin's keys are among the kq
+          sh_bin_cnt = h;
+          break;
+        }
+        a += h;
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = (uint32_t)sh_bin;
+    const int rem = sh_bin_rem, cnt = sh_bin_cnt;
+    if (cnt <= 256) {
+#pragma unroll
+      for (int u = 0; u < kSmallPer; ++u)
+        if (in[u] && (key[u] >> 20) == bin) cand[atomicAdd(&sh_cnt, 1)] = key[u];
+      __syncthreads();
+      if (tid < cnt) {
+        const uint32_t y = cand[tid];
+        int gt = 0, ge = 0;
+#pragma unroll 8
+        for (int c = 0; c < cnt; ++c) {
+          const uint32_t z = cand[c];
+          gt += z > y ? 1 : 0;
+          ge += z >= y ? 1 : 0;
+        }
+        if (gt < rem && rem <= ge) {  // y is the rem-th largest of the bin (equal keys write equal values)
+          sh_prefix = y;
+          sh_rem = rem - gt;
+        }
+      }
+      __syncthreads();
+      thr = sh_prefix;
+      need_eq = sh_rem;
+    } else {
+      // heavy ties or clustering: an exact 8-bit radix select over the keys in LDS
+#pragma unroll
+      for (int u = 0; u < kSmallPer; ++u)
+        if (in[u]) keys[u * 256 + tid - sink_hi] = key[u];
+      __syncthreads();
+      radix_select(
+          ncand, kq, [&](int i) { return keys[i]; }, [](int) { return true; }, hist, scan4, &sh_prefix, &sh_rem,
+          thr, need_eq);
+    }
+  }
+
+  // per round: keys above the threshold (every candidate when nothing is
+  // ranked, none when k = 0) and keys equal to it, counted per wave
+  bool gtf[kSmallPer], eqf[kSmallPer];
+  int gi[kSmallPer], ei[kSmallPer];
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) {
+    gtf[u] = kq > 0 && in[u] && (!ranked || key[u] > thr);
+    eqf[u] = ranked && in[u] && key[u] == thr;
+    gi[u] = wave_incl_sum(gtf[u] ? 1 : 0);
+    ei[u] = wave_incl_sum(eqf[u] ? 1 : 0);
+    if (lane == 63) {
+      counts[0][u][w] = gi[u];
+      counts[1][u][w] = ei[u];
+    }
+  }
+  __syncthreads();
+  int gt_base = 0, eq_base = 0;  // keys above / equal in the rounds before u
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) {
+    int g_before = gt_base + gi[u] - (gtf[u] ? 1 : 0), e_before = eq_base + ei[u] - (eqf[u] ? 1 : 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int gv = counts[0][u][v], ev = counts[1][u][v];
+      g_before += v < w ? gv : 0;
+      e_before += v < w ? ev : 0;
+      gt_base += gv;
+      eq_base += ev;
+    }
+    if (gtf[u] || (eqf[u] && e_before < need_eq)) {
+      const int o = sink_hi + g_before + min(e_before, need_eq);
+      if (o < max_sel) out[o] = u * 256 + tid;
+    }
+  }
+  const int npick = gt_base + (ranked ? need_eq : 0);
+  for (int j = tid; j < sink_hi; j += 256)
+    if (j < max_sel) out[j] = j;
+  for (int j = rec_lo + tid; j < nb; j += 256) {
+    const int o = sink_hi + npick + (j - rec_lo);
+    if (o < max_sel) out[o] = j;
+  }
+  const int total = sink_hi + npick + (nb - rec_lo);
+  for (int o = total + tid; o < max_sel; o += 256) out[o] = -1;
+  if (tid == 0) n_sel[unit] = min(total, max_sel);
+}
+
 // ---- importance order: one workgroup per (b, kv head) -------------------
 // Block 0 first, then blocks 1 .. nb-1 by descending score, lower index first
 // among equal scores ("ART" summary, §2.4, importance-first visit order).
@@ -721,8 +886,12 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int32_t B, 
                        int32_t NBmax, int32_t k, int32_t n_sink, int32_t n_recent,
                        int32_t max_sel, int32_t* idx, int32_t* n_sel, hipStream_t st) {
   if (B == 0) return hipSuccess;
-  topk_kernel<<<dim3(B * Hkv), 256, 0, st>>>(scores, seq_lens, Hkv, NBmax, k, n_sink, n_recent,
-                                             max_sel, idx, n_sel);
+  if (NBmax <= kTopkSmall)
+    topk_small_kernel<<<dim3(B * Hkv), 256, 0, st>>>(scores, seq_lens, Hkv, NBmax, k, n_sink, n_recent, max_sel,
+                                                     idx, n_sel);
+  else
+    topk_kernel<<<dim3(B * Hkv), 256, 0, st>>>(scores, seq_lens, Hkv, NBmax, k, n_sink, n_recent, max_sel, idx,
+                                               n_sel);
   return hipGetLastError();
 }
 
