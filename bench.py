@@ -775,17 +775,19 @@ def run_ceiling(reps=10):
     return dict(kernel="stream_read_kernel (non-temporal 16-byte loads, whole lines)", bytes=nbytes,
                 gbs=sweep[best], pct_peak=100 * sweep[best] / PEAK_HBM_GBS, workgroups=best,
                 sweep_gbs={str(k_): round(v_, 1) for k_, v_ in sweep.items()},
-                launch_us=run_launch_floor(lib, sink))
+                launch_us=run_launch_floor(lib, sink, "skv_bench_empty"),
+                launch_with_stores_us=run_launch_floor(lib, sink, "skv_bench_store"))
 
 
-def run_launch_floor(lib, sink, launches=200, reps=10):
-    """Fixed cost per kernel launch: a chain of empty 256-workgroup launches captured in a HIP graph,
-    replayed and timed with events; the median time per launch, in microseconds."""
+def run_launch_floor(lib, sink, probe, launches=200, reps=10):
+    """Fixed cost per kernel launch: a chain of 256-workgroup launches of a probe kernel (empty, or one store
+    per thread) captured in a HIP graph, replayed and timed with events; the median time per launch, in
+    microseconds."""
     import ctypes
 
     import torch
 
-    f = lib.skv_bench_empty
+    f = getattr(lib, probe)
     f.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     f.restype = ctypes.c_int
 
@@ -793,7 +795,7 @@ def run_launch_floor(lib, sink, launches=200, reps=10):
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         for _ in range(launches):
             if f(256, ctypes.c_void_p(sink.data_ptr()), stream) != 0:
-                raise RuntimeError("skv_bench_empty failed")
+                raise RuntimeError(f"{probe} failed")
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

@@ -37,6 +37,14 @@ int skv_bench_stream_read(const void* buf, size_t bytes, int32_t workgroups, uin
  */
 int skv_bench_empty(int32_t workgroups, uint32_t* sink, void* stream);
 
+/*
+ * Queue one launch of a kernel whose only work is one 4-byte store per thread
+ * (`workgroups` workgroups of 256 threads) into `sink`, device uint32
+ * [workgroups * 256].  A chain of these gives the fixed cost of a launch that
+ * writes memory.  Returns 0, -1 on invalid arguments, -3 when the launch fails.
+ */
+int skv_bench_store(int32_t workgroups, uint32_t* sink, void* stream);
+
 #pragma GCC visibility pop
 
 #ifdef __cplusplus

@@ -60,7 +60,20 @@ __global__ __launch_bounds__(kThreads) void empty_kernel(uint32_t* sink, uint32_
   if (never == 0x9E3779B9u) sink[blockIdx.x * kThreads + threadIdx.x] = never;
 }
 
+// The same with one 4-byte store per thread: a dependent chain of these takes
+// the fixed cost of a launch that writes memory (its stores drain before the
+// next launch starts).
+__global__ __launch_bounds__(kThreads) void store_kernel(uint32_t* sink) {
+  sink[blockIdx.x * kThreads + threadIdx.x] = blockIdx.x;
+}
+
 }  // namespace
+
+extern "C" int skv_bench_store(int32_t workgroups, uint32_t* sink, void* stream) {
+  if (!sink || workgroups < 1) return -1;
+  store_kernel<<<workgroups, kThreads, 0, (hipStream_t)stream>>>(sink);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 extern "C" int skv_bench_empty(int32_t workgroups, uint32_t* sink, void* stream) {
   if (!sink || workgroups < 1) return -1;

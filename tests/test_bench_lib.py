@@ -24,7 +24,12 @@ def blib():
 def test_exports_and_validation(blib):
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     names = set(re.findall(r"^\s*int\s+(skv_[a-z_]+)\s*\(", text, flags=re.M))
-    assert names == {"skv_bench_stream_read", "skv_bench_empty"}
+    assert names == {"skv_bench_stream_read", "skv_bench_empty", "skv_bench_store"}
+    st = blib.skv_bench_store
+    st.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    st.restype = ctypes.c_int
+    assert st(256, None, None) == -1
+    assert st(0, ctypes.c_void_p(0x1000), None) == -1
     e = blib.skv_bench_empty
     e.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     e.restype = ctypes.c_int
