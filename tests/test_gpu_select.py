@@ -67,11 +67,13 @@ def test_topk_exact_on_given_scores(k, ns, nr):
 
 @pytest.mark.parametrize("NB", [2048, 4096])
 def test_topk_large_rows_radix_paths(NB):
-    # 2048-block rows take the one-wave register select, longer rows the workgroup radix select
+    # rows of up to 2048 blocks take the register-resident select, longer rows the LDS-staged one;
+    # in both, the 8-bit radix select takes over when the k-th key's 12-bit bin holds over 256 keys
     log(f"[select] top-k on {NB}-block rows")
     r = np.random.default_rng(9)
     B, Hkv = 2, 2
     s = (r.standard_normal((B, Hkv, NB)) * 3).astype(np.float32)
+    s[0, 0] = (1.0 + r.integers(0, 3000, NB) * 1e-7).astype(np.float32)  # one 12-bit bin, with ties
     s[0, 1] = np.round(s[0, 1] * 4) / 4  # heavy ties
     s[1, 0, 100:200] = s[1, 0, NB * 3 // 4]  # ties at the boundary region
     s[1, 1, 7] = -0.0
