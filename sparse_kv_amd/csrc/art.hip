@@ -642,6 +642,14 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int f, int b, i
       continue;
     }
     ring.acquire();
+    // the output rows of the batch's first chunk, in flight with its states
+    // and through the scan; later chunks are read in the fold
+    constexpr int CK0 = (64 / FE < 32 ? 64 / FE : 32) < NBT ? (64 / FE < 32 ? 64 / FE : 32) : NBT;
+    constexpr int CK = CK0 < GS ? GS : CK0;
+    static_assert(CK % GS == 0, "chunks of whole groups");
+    float x0[CK][FE];
+#pragma unroll
+    for (int jj = 0; jj < CK; ++jj) ring.acc_row((t0 + min(jj, n - 1)) % kR, head, j * FE, x0[jj]);
     const bool in = live && j < n;
     const int s = tj % kR;
     float m = -INFINITY, l = 0.f, a[PW];
@@ -743,13 +751,17 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int f, int b, i
     {
       // chunks of positions whose rows are all loaded before any is used;
       // positions past the batch reread its last slot with weight 0
-      constexpr int CK0 = (64 / FE < 32 ? 64 / FE : 32) < NBT ? (64 / FE < 32 ? 64 / FE : 32) : NBT;
-      constexpr int CK = CK0 < GS ? GS : CK0;
-      static_assert(CK % GS == 0, "chunks of whole groups");
       for (int j0 = 0; j0 < n; j0 += CK) {
         float x[CK][FE];
 #pragma unroll
-        for (int jj = 0; jj < CK; ++jj) ring.acc_row((t0 + min(j0 + jj, n - 1)) % kR, head, j * FE, x[jj]);
+        for (int jj = 0; jj < CK; ++jj) {
+          if (j0 == 0) {
+#pragma unroll
+            for (int e = 0; e < FE; ++e) x[jj][e] = x0[jj][e];
+          } else {
+            ring.acc_row((t0 + min(j0 + jj, n - 1)) % kR, head, j * FE, x[jj]);
+          }
+        }
 #pragma unroll
         for (int jj = 0; jj < CK; ++jj) {
           if (jj % GS == 0 && j0 + jj < n) {
