@@ -137,20 +137,15 @@ struct LdsRing {
   }
 };
 
-// In global memory: the workgroups of one (b, kv head), on different CUs of
-// one XCD (the unit's home: workgroups that find themselves on another XCD
-// take no part).  Stores, position and count reads and the accounting
-// atomics are device-scope ones: stores write through to the device's
-// coherence point and those loads read from it, so no wave ever writes back
-// or invalidates a whole L2 (with hundreds of producer waves doing so per
-// block, that costs tens of microseconds a block), and late workgroups on
-// any XCD read the folded counts right.  The folders' block-state loads are
-// L2-scope (sc0: past the CU's L1, served by the XCD's L2): every state was
-// stored, through that same L2, by a producer on the home XCD.  Order comes
-// from completion: a producer waits for its state stores to complete before
-// it stores the position, the folder issues its state loads only after it
-// has read the position, and it waits for them to complete before it
-// advances the window.
+// In global memory: the workgroups of one (b, kv head), on different CUs
+// and, in general, different XCDs.  Every access to the ring is a
+// device-scope one: stores write through to the device's coherence point
+// and loads read from it, so no wave ever writes back or invalidates a whole
+// L2 (with hundreds of producer waves doing so per block, that costs tens
+// of microseconds a block).  Order comes from completion: a producer waits
+// for its state stores to complete before it stores the position, the
+// folder issues its state loads only after it has read the position, and it
+// waits for them to complete before it advances the window.
 template <int GP, int D, int R, int NF, int EP = 4>
 struct GlobalRing {
   static constexpr int kR = R;
@@ -158,7 +153,7 @@ struct GlobalRing {
   // control words, on separate 128-byte lines: the folders' counts of
   // folded positions (polled by every producer), the position claims, the
   // accounting words
-  enum Ctrl { kFolded = 0, kNext = 32, kFetched = 64, kFolder, kHome, kNumCtrl = 96 };
+  enum Ctrl { kFolded = 0, kNext = 32, kFetched = 64, kFolder, kNumCtrl = 96 };
   static_assert(NF <= 8 && R * 4 <= 512, "control and position areas");
   static constexpr uint32_t kPosOff = 0, kCtrlOff = 512;
   static constexpr uint32_t kMOff = kCtrlOff + 512;
@@ -171,9 +166,6 @@ struct GlobalRing {
   int* ctrl;
   __amdgpu_buffer_rsrc_t rs;
   int* local_fetched = nullptr;  // this workgroup's fetch count (LDS)
-  // cache policy of the block-state loads (folders only): L2 scope (sc0) --
-  // every producer of a unit runs on the folder's XCD and writes through its L2
-  static constexpr int ld = 1;
   __device__ GlobalRing(char* ws, int unit) {
     char* u = ws + (size_t)unit * kBytes;
     pos = (int*)(u + kPosOff);
@@ -203,14 +195,14 @@ struct GlobalRing {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv), rs, (int)kLOff + o, 0, kSc1);
   }
   __device__ f32x4 acc4(int s, int q, int col) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)acc_off(s, q, col), 0, ld);
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)acc_off(s, q, col), 0, kSc1);
     return f32x4{__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3])};
   }
   __device__ float m_at(int s, int q) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)kMOff + (s * GP + q) * 4, 0, ld));
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)kMOff + (s * GP + q) * 4, 0, kSc1));
   }
   __device__ float l_at(int s, int q) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)kLOff + (s * GP + q) * 4, 0, ld));
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)kLOff + (s * GP + q) * 4, 0, kSc1));
   }
   // vmcnt(0), with no memory access moved across it by the compiler
   static __device__ void wait_memory() {
@@ -244,12 +236,12 @@ struct GlobalRing {
         for (int i = 0; i < 4; ++i) x[e + i] = v[i];
       }
     } else if constexpr (FE == 2) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)acc_off(s, q, col), 0, ld);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)acc_off(s, q, col), 0, kSc1);
       x[0] = __uint_as_float(v[0]);
       x[1] = __uint_as_float(v[1]);
     } else {
       static_assert(FE == 1, "row slice of 1, 2 or 4k floats");
-      x[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)acc_off(s, q, col), 0, ld));
+      x[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)acc_off(s, q, col), 0, kSc1));
     }
   }
   __device__ int poll(int s) { return __hip_atomic_load(&pos[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
@@ -855,12 +847,9 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_kernel(ArtArgs p) {
 // Several workgroups per (b, kv head) unit, for grids that would leave most
 // CUs idle: one CU streams well under its share of HBM bandwidth, so a unit
 // on one CU is bound by that CU.  The unit's workgroups share a ring in
-// global memory; the first workgroup to arrive sets the unit's home XCD
-// (its own; a unit's first workgroups, blockIdx u + k * units, are
-// dispatched to one XCD) and workgroups on other XCDs leave; the first wave 0
-// of a home workgroup folds, the other wave 0s leave, and every producer
-// wave claims positions from the unit's counter, so progress never depends
-// on which workgroups are resident.  The grid holds
+// global memory; the first wave 0 to arrive folds, the other wave 0s leave,
+// and every producer wave claims positions from the unit's counter, so
+// progress never depends on which workgroups are resident.  The grid holds
 // `groups` workgroups per unit, then late workgroups: each of those joins a
 // unit whose folders are still at work when it starts (units stop at very
 // different positions, and these add producers to the ones still running
@@ -895,20 +884,10 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* 
   using RING = GlobalRing<4 * GR, D, R, NF, Geo<T, D>::E>;
   __shared__ SH sh;
   const int units = p.B * p.Hkv;
-  // first workgroups: those dispatched to one XCD (blockIdx mod 8, round
-  // robin) take units x, x + 8, ... in turn, `groups` workgroups each, so a
-  // unit's first workgroups share an XCD; the ones past the last unit, and
-  // the late ones, look for a unit
-  const int bx = (int)blockIdx.x;
-  int unit = (bx / 8 / groups) * 8 + bx % 8;
-  unsigned xcc_reg;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc_reg));
-  const int xcc = (int)(xcc_reg & 0xF) + 1;  // this workgroup's XCD, 1-based (0: no home yet)
-  if (bx >= units * groups || unit >= units) {
-    unit = bx % units;
+  int unit = (int)blockIdx.x % units;
+  if ((int)blockIdx.x >= units * groups) {
     // a late workgroup: the first unit, from its own on, whose folders have
-    // not all finished and whose home is this XCD (units <= 128: two looks
-    // per lane at most)
+    // not all finished (units <= 128: two looks per lane at most)
     if (threadIdx.x < 64) {
       const int lane = threadIdx.x;
       int pick = -1;
@@ -921,8 +900,7 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* 
 #pragma unroll
           for (int f = 0; f < NF; ++f)
             done += __hip_atomic_load(&r.ctrl[RING::kFolded + f], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= kDoneMark;
-          active = done < NF &&
-                   __hip_atomic_load(&r.ctrl[RING::kHome], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == xcc;
+          active = done < NF;
         }
         const uint64_t act = (uint64_t)__ballot(active);
         if (act) pick = (unit + base + (int)__builtin_ctzll(act)) % units;
@@ -943,16 +921,9 @@ __global__ __launch_bounds__((NP + 1) * 64) void art_mc_kernel(ArtArgs p, char* 
   RING ring(ws, unit);
   if (threadIdx.x == 0) {
     sh.fetched = 0;
-    // the unit's home XCD: the first workgroup's; only workgroups on it take part
-    int home = 0;
-    __hip_atomic_compare_exchange_strong(&ring.ctrl[RING::kHome], &home, xcc, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    const bool on_home = home == 0 || home == xcc;
-    sh.role = on_home ? __hip_atomic_fetch_add(&ring.ctrl[RING::kFolder], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                      : -1;
+    sh.role = __hip_atomic_fetch_add(&ring.ctrl[RING::kFolder], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  if (sh.role < 0) return;  // the whole workgroup: another XCD's unit
   ring.local_fetched = &sh.fetched;
   const bool folds = sh.role == 0;
   if (folds && w < NF) {
