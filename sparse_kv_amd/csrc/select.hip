@@ -176,6 +176,11 @@ __device__ __forceinline__ int wave_incl_sum(int x) {
   return x;
 }
 
+// Number of lanes below this one whose bit is set in a wave-wide mask.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Exclusive prefix sum of one int per thread over a 256-thread workgroup.
 __device__ int block_exscan(int x, int* total, int* lds4) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -258,6 +263,44 @@ __device__ void radix_select(int n, int kk, KeyF key, EligF elig, uint32_t* hist
   need_eq = rem;
 }
 
+// The bin of a 4096-bin histogram (top 12 bits of the keys) that holds the
+// kk-th largest key.  Thread t owns bins 4095 - 16 t - c (c = 0..15), read
+// as four 16-byte loads into registers (hist must be 16-byte aligned); a
+// block scan gives the keys in the bins above each thread's, and the one
+// thread whose bins take the running count from below kk to at least kk
+// returns true with the bin, how many of its keys are among the kk (rem) and
+// its count.  Every thread of the workgroup must call it.
+__device__ bool kth_bin(const uint32_t* hist, int kk, int* scan4, int& bin, int& rem, int& cnt) {
+  const int tid = threadIdx.x;
+  uint32_t hb[16];  // hb[15 - c] is bin 4095 - 16 t - c
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 h4 = *(const u32x4*)&hist[4080 - 16 * tid + 4 * i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hb[4 * i + e] = h4[e];
+  }
+  int loc = 0;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) loc += (int)hb[c];
+  int tot;
+  const int above = block_exscan(loc, &tot, scan4);  // keys in the bins above this thread's
+  if (!(above < kk && kk <= above + loc)) return false;
+  int a = above, fc = 0, fa = above, fh = 0;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {  // downwards; exactly one bin crosses kk
+    const int h = (int)hb[15 - c];
+    const bool here = a < kk && a + h >= kk;
+    fc = here ? c : fc;
+    fa = here ? a : fa;
+    fh = here ? h : fh;
+    a += h;
+  }
+  bin = 4095 - 16 * tid - fc;
+  rem = kk - fa;
+  cnt = fh;
+  return true;
+}
+
 // The kk-th largest key in one histogram pass, for keys cheap to read twice
 // (staged in LDS): a 4096-bin histogram of the top 12 key bits locates the
 // bin holding it (thread t sums bins 4095 - 16t ...; one block scan), then
@@ -276,23 +319,12 @@ __device__ bool select_wide(int n, int kk, KeyF key, EligF elig, uint32_t* hist,
   for (int i = tid; i < n; i += 256)
     if (elig(i)) atomicAdd(&hist[key(i) >> 20], 1u);
   __syncthreads();
-  int loc = 0;
-#pragma unroll
-  for (int c = 0; c < 16; ++c) loc += (int)hist[4095 - 16 * tid - c];
-  int tot;
-  const int above = block_exscan(loc, &tot, scan4);  // keys in the bins above this thread's
-  if (above < kk && kk <= above + loc) {
-    int a = above;
-    for (int c = 0; c < 16; ++c) {
-      const int bin = 4095 - 16 * tid - c;
-      const int h = (int)hist[bin];
-      if (a + h >= kk) {
-        sh[0] = bin;
-        sh[1] = kk - a;  // how many of the bin's keys are among the kk
-        sh[2] = h;
-        break;
-      }
-      a += h;
+  {
+    int fb, fr, fn;
+    if (kth_bin(hist, kk, scan4, fb, fr, fn)) {
+      sh[0] = fb;
+      sh[1] = fr;  // how many of the bin's keys are among the kk
+      sh[2] = fn;
     }
   }
   if (tid == 0) sh[3] = 0;
@@ -300,8 +332,20 @@ __device__ bool select_wide(int n, int kk, KeyF key, EligF elig, uint32_t* hist,
   const uint32_t bin = (uint32_t)sh[0];
   const int rem = sh[1], cnt = sh[2];
   if (cnt > 256) return false;
-  for (int i = tid; i < n; i += 256)
-    if (elig(i) && (key(i) >> 20) == bin) cand[atomicAdd(&sh[3], 1)] = key(i);
+  // the bin's keys, in any order (the rank below does not depend on it); one
+  // atomic per wave and pass reserves room for the wave's keys
+  const int lane = tid & 63;
+  for (int i0 = 0; i0 < n; i0 += 256) {
+    const int i = i0 + tid;
+    const bool m = i < n && elig(i) && (key(i) >> 20) == bin;
+    const uint64_t mk = (uint64_t)__ballot(m);
+    if (mk != 0) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sh[3], __popcll(mk));
+      base = __shfl(base, 0);
+      if (m) cand[base + lanes_below(mk)] = key(i);
+    }
+  }
   __syncthreads();
   if (tid < cnt) {
     const uint32_t x = cand[tid];
@@ -399,7 +443,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
                                                    int32_t n_recent, int32_t max_sel, int32_t* __restrict__ idx,
                                                    int32_t* __restrict__ n_sel) {
   __shared__ uint32_t keys[kTopkStage];
-  __shared__ uint32_t hist[4096];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4096];
   __shared__ uint32_t cand[256];
   __shared__ int scan4[4];
   __shared__ uint32_t sh_prefix;
@@ -481,7 +525,7 @@ __global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict
                                                          int32_t max_sel, int32_t* __restrict__ idx,
                                                          int32_t* __restrict__ n_sel) {
   __shared__ uint32_t keys[kTopkSmall];  // the radix select's copy of the keys
-  __shared__ uint32_t hist[4096];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4096];
   __shared__ uint32_t cand[256];
   __shared__ int scan4[4];
   __shared__ int counts[2][kSmallPer][4];  // per round and wave: keys above, and equal to, the k-th key
@@ -527,32 +571,35 @@ __global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict
     for (int u = 0; u < kSmallPer; ++u)
       if (in[u]) atomicAdd(&hist[key[u] >> 20], 1u);
     __syncthreads();
-    int loc = 0;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) loc += (int)hist[4095 - 16 * tid - c];
-    int tot;
-    const int above = block_exscan(loc, &tot, scan4);  // keys in the bins above this thread's
-    if (above < kq && kq <= above + loc) {
-      int a = above;
-      for (int c = 0; c < 16; ++c) {
-        const int bin = 4095 - 16 * tid - c;
-        const int h = (int)hist[bin];
-        if (a + h >= kq) {
-          sh_bin = bin;
-          sh_bin_rem = kq - a;  // how many of the bin's keys are among the kq
-          sh_bin_cnt = h;
-          break;
-        }
-        a += h;
+    {
+      int fb, fr, fn;
+      if (kth_bin(hist, kq, scan4, fb, fr, fn)) {
+        sh_bin = fb;
+        sh_bin_rem = fr;  // how many of the bin's keys are among the kq
+        sh_bin_cnt = fn;
       }
     }
     __syncthreads();
     const uint32_t bin = (uint32_t)sh_bin;
     const int rem = sh_bin_rem, cnt = sh_bin_cnt;
     if (cnt <= 256) {
+      // the bin's keys, in any order (the rank below does not depend on it):
+      // one atomic per wave reserves room for the wave's keys of every round
+      uint64_t mk[kSmallPer];
+      int wtot = 0;
 #pragma unroll
-      for (int u = 0; u < kSmallPer; ++u)
-        if (in[u] && (key[u] >> 20) == bin) cand[atomicAdd(&sh_cnt, 1)] = key[u];
+      for (int u = 0; u < kSmallPer; ++u) {
+        mk[u] = (uint64_t)__ballot(in[u] && (key[u] >> 20) == bin);
+        wtot += __popcll(mk[u]);
+      }
+      int base = 0;
+      if (lane == 0 && wtot > 0) base = atomicAdd(&sh_cnt, wtot);
+      base = __shfl(base, 0);
+#pragma unroll
+      for (int u = 0; u < kSmallPer; ++u) {
+        if ((mk[u] >> lane) & 1) cand[base + lanes_below(mk[u])] = key[u];
+        base += __popcll(mk[u]);
+      }
       __syncthreads();
       if (tid < cnt) {
         const uint32_t y = cand[tid];
@@ -586,23 +633,24 @@ __global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict
   // per round: keys above the threshold (every candidate when nothing is
   // ranked, none when k = 0) and keys equal to it, counted per wave
   bool gtf[kSmallPer], eqf[kSmallPer];
-  int gi[kSmallPer], ei[kSmallPer];
+  int gi[kSmallPer], ei[kSmallPer];  // the wave's lanes below this one with the flag
 #pragma unroll
   for (int u = 0; u < kSmallPer; ++u) {
     gtf[u] = kq > 0 && in[u] && (!ranked || key[u] > thr);
     eqf[u] = ranked && in[u] && key[u] == thr;
-    gi[u] = wave_incl_sum(gtf[u] ? 1 : 0);
-    ei[u] = wave_incl_sum(eqf[u] ? 1 : 0);
-    if (lane == 63) {
-      counts[0][u][w] = gi[u];
-      counts[1][u][w] = ei[u];
+    const uint64_t gm = (uint64_t)__ballot(gtf[u]), em = (uint64_t)__ballot(eqf[u]);
+    gi[u] = lanes_below(gm);
+    ei[u] = lanes_below(em);
+    if (lane == 0) {
+      counts[0][u][w] = __popcll(gm);
+      counts[1][u][w] = __popcll(em);
     }
   }
   __syncthreads();
   int gt_base = 0, eq_base = 0;  // keys above / equal in the rounds before u
 #pragma unroll
   for (int u = 0; u < kSmallPer; ++u) {
-    int g_before = gt_base + gi[u] - (gtf[u] ? 1 : 0), e_before = eq_base + ei[u] - (eqf[u] ? 1 : 0);
+    int g_before = gt_base + gi[u], e_before = eq_base + ei[u];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int gv = counts[0][u][v], ev = counts[1][u][v];
