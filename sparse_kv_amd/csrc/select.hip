@@ -680,7 +680,8 @@ __global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict
 // Block 0 first, then blocks 1 .. nb-1 by descending score, lower index first
 // among equal scores ("ART" summary, §2.4, importance-first visit order).
 // The nb - 1 keys (inverted score key << 32 | block) are sorted ascending by
-// a bitonic network in LDS, padded to a power of two with all-ones keys.
+// a bitonic network in LDS, padded to a power of two with all-ones keys;
+// stages whose partners lie within one wave's keys run without a barrier.
 template <int CAP>
 __global__ __launch_bounds__(1024) void order_kernel(const float* __restrict__ scores,
                                                      const int32_t* __restrict__ seq_lens, int32_t Hkv,
@@ -697,20 +698,34 @@ __global__ __launch_bounds__(1024) void order_kernel(const float* __restrict__ s
   for (int i = tid; i < n; i += 1024)
     key[i] = i < nr ? ((uint64_t)~score_key(row[i + 1]) << 32) | (uint32_t)(i + 1) : ~(uint64_t)0;
   __syncthreads();
-  for (int kk = 2, lk = 1; kk <= n; kk <<= 1, ++lk) {
-    for (int j = kk >> 1, lj = lk - 1; j > 0; j >>= 1, --lj) {
-      for (int pr = tid; pr < (n >> 1); pr += 1024) {
-        // pair (i, i + j) with i = 2 j floor(pr / j) + pr mod j; j = 2^lj
-        const int i = ((pr >> lj) << (lj + 1)) | (pr & (j - 1));
-        const uint64_t x = key[i], y = key[i + j];
-        const bool up = (i & kk) == 0;
-        if ((x > y) == up) {
-          key[i] = y;
-          key[i + j] = x;
-        }
+  // one compare-exchange stage: pair (i, i + j) with i = 2 j floor(pr / j) +
+  // pr mod j, j = 2^lj
+  auto stage = [&](int kk, int j, int lj) {
+    for (int pr = tid; pr < (n >> 1); pr += 1024) {
+      const int i = ((pr >> lj) << (lj + 1)) | (pr & (j - 1));
+      const uint64_t x = key[i], y = key[i + j];
+      const bool up = (i & kk) == 0;
+      if ((x > y) == up) {
+        key[i] = y;
+        key[i + j] = x;
       }
+    }
+  };
+  for (int kk = 2, lk = 1; kk <= n; kk <<= 1, ++lk) {
+    int j = kk >> 1, lj = lk - 1;
+    // partners 64 or more apart may belong to other waves: a barrier a stage
+    for (; j >= 64; j >>= 1, --lj) {
+      stage(kk, j, lj);
       __syncthreads();
     }
+    // closer partners: the 32 pairs pr = 32 c .. 32 c + 31 of a wave cover the
+    // aligned 64 keys 64 c .. 64 c + 63 for every j <= 32, so the rest of this
+    // merge needs no workgroup barrier
+    for (; j > 0; j >>= 1, --lj) {
+      stage(kk, j, lj);
+      wave_lds_exchange();
+    }
+    __syncthreads();
   }
   for (int i = tid; i < NBmax; i += 1024)
     out[i] = i == 0 ? (nb > 0 ? 0 : -1) : (i < nb ? (int32_t)(uint32_t)key[i - 1] : -1);

@@ -1,8 +1,9 @@
 """GPU: a whole decode step (dense + merge, scores + top-k + listed-block decode
 + merge, ART across workgroups, sink + window) captured once in a HIP graph and
 replayed with new query data each time; every replay must equal the eager
-calls on the same data (the library queues no memset and allocates nothing
-inside the calls that take their outputs and workspaces)."""
+calls on the same data bit for bit (the library queues no memset and
+allocates nothing inside the calls that take their outputs and workspaces,
+and every entry point, the multi-workgroup ART included, is reproducible)."""
 
 import numpy as np
 import pytest
@@ -46,9 +47,7 @@ def test_decode_step_graph_replays_match_eager():
                              n_sel=nsel)
         skv.attn_decode_sparse(q, k, v, sel, nsel, sl, num_splits=S, m=st[1][0], l=st[1][1], o=st[1][2])
         skv.attn_merge_states(*st[1], out=outs[1])
-        # tau = phi = 0: no stop, so the stop positions are the same however the
-        # folders' batches fall (the fold's rounding may differ by ~1e-7)
-        skv.attn_decode_art_ws(q, k, v, sl, tau=0.0, phi=0.0, patience=2, probe_dim=8, workspace=ws,
+        skv.attn_decode_art_ws(q, k, v, sl, tau=2e-2, phi=2e-3, patience=2, probe_dim=8, workspace=ws,
                                out=outs[2], stop_pos=stop)
         skv.attn_decode_sparse(q, k, v, win, nwin, sl, num_splits=S, m=st[2][0], l=st[2][1], o=st[2][2])
         skv.attn_merge_states(*st[2], out=outs[3])
@@ -81,5 +80,4 @@ def test_decode_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         got = snapshot()
         for i, (a, b) in enumerate(zip(got, want)):
-            assert torch.equal(a, b) or (a.dtype == torch.float32 and float((a - b).abs().max()) <= 1e-6), \
-                (rep, i, float((a.float() - b.float()).abs().max()))
+            assert torch.equal(a, b), (rep, i, float((a.float() - b.float()).abs().max()))
