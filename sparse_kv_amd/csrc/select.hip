@@ -513,9 +513,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
 // a time.  The k-th key comes from the 4096-bin histogram of the top 12 key
 // bits and the rank of the <= 256 keys in its bin, as in select_wide (an
 // 8-bit radix select over the keys staged in LDS when the bin holds more).
-// The chosen blocks are compacted in block order from per-round prefix
-// counts: block 256 u + t follows every block of rounds before u and the
-// blocks of round u held by lower threads.
+// The chosen blocks are compacted in block order from per-round counts
+// (wave ballots, then per-wave totals): block 256 u + t follows every block
+// of rounds before u and the blocks of round u held by lower threads.
 constexpr int kTopkSmall = 2048;
 constexpr int kSmallPer = kTopkSmall / 256;
 
