@@ -762,16 +762,26 @@ __device__ void art_folder(const ArtArgs& p, SH& sh, RING& ring, int f, int b, i
             ring.acc_row((t0 + min(j0 + jj, n - 1)) % kR, head, j * FE, x[jj]);
           }
         }
+        // the chunk's weights and group rescales, read from LDS together
+        // (16-byte loads) before any is used; positions past the batch
+        // carry weight 0 and groups past it rescale by 1
+        float wt[CK], ga[CK / GS];
+#pragma unroll
+        for (int jj = 0; jj < CK; jj += 4) {
+          const f32x4 w4 = *(const f32x4*)&fold_w[hh * CH + j0 + jj];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wt[jj + e] = j0 + jj + e < n ? w4[e] : 0.f;
+        }
+#pragma unroll
+        for (int gg = 0; gg < CK / GS; ++gg) ga[gg] = fold_a[hh * (CH / GS) + j0 / GS + gg];
 #pragma unroll
         for (int jj = 0; jj < CK; ++jj) {
           if (jj % GS == 0 && j0 + jj < n) {
-            const float al = fold_a[hh * (CH / GS) + (j0 + jj) / GS];
 #pragma unroll
-            for (int e = 0; e < FE; ++e) A[e] *= al;
+            for (int e = 0; e < FE; ++e) A[e] *= ga[jj / GS];
           }
-          const float w = j0 + jj < n ? fold_w[hh * CH + j0 + jj] : 0.f;
 #pragma unroll
-          for (int e = 0; e < FE; ++e) A[e] = fmaf(w, x[jj][e], A[e]);
+          for (int e = 0; e < FE; ++e) A[e] = fmaf(wt[jj], x[jj][e], A[e]);
         }
       }
     }
