@@ -151,3 +151,37 @@ def test_shard_aligned_two_level_merge_equals_one_level():
     assert_close(two.cpu().numpy(), one.cpu().numpy(), 2e-6, "two-level vs one-level")
     qf, kf, vf = inp.f64()
     assert_close(two.cpu().numpy(), oracle.decode_dense(qf, kf, vf, inp.seq_lens, inp.scale), TOL, "vs oracle")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_routed_sweep_matches_oracle(seed):
+    """A seeded sweep of routed stacks: layer count and route mask, shard and split counts (including
+    rows with more than 64 states, merged in two launches), sink and window sizes, group size, head
+    dim, ragged rows; sink + window layers poisoned outside their blocks."""
+    import sparse_kv_amd as skv
+
+    r = np.random.default_rng(4000 + seed)
+    n_layers = int(r.integers(1, 6))
+    mask = [int(x) for x in r.integers(0, 2, n_layers)]
+    B, Hkv = int(r.integers(1, 4)), int(r.integers(1, 3))
+    G, d = int(r.choice([1, 2, 4, 8])), int(r.choice([64, 128]))
+    NB = int(r.integers(2, 41))
+    seq = [int(x) for x in r.integers(0, 64 * NB + 1, B)]
+    seq[0] = 64 * NB
+    n_shards, sps, sa_splits = int(r.integers(1, 10)), int(r.integers(1, 9)), int(r.integers(1, 33))
+    if seed % 5 == 4:
+        n_shards, sps = 9, 8  # 72 states per row
+    n_sink, n_recent = int(r.integers(0, 3)), int(r.integers(0, 12))
+    log(f"[routed] sweep seed={seed}: mask {mask}, B={B} Hq={G * Hkv} Hkv={Hkv} d={d} seq={seq}, "
+        f"{n_shards} shards x {sps} splits, {sa_splits} SA splits, sink {n_sink}, window {n_recent}")
+    layers, host, L = _stack(60 + seed, mask, B, G * Hkv, Hkv, d, seq, n_sink, n_recent)
+    sl = layers[0][3]
+    idx, n = skv.attn_select_topk(None, sl, k=0, n_sink_blocks=n_sink, n_recent_blocks=n_recent,
+                                  shape=(B, Hkv, L // 64))
+    outs = skv.attn_decode_routed([x[0] for x in layers], [x[1] for x in layers], [x[2] for x in layers], mask,
+                                  sl, n_shards=n_shards, splits_per_shard=sps, sa_block_idx=idx, sa_n_sel=n,
+                                  sa_splits=sa_splits)
+    torch.cuda.synchronize()
+    ref = oracle.routed_layer_outputs(host, np.array(seq), 1 / np.sqrt(d), mask, n_sink, n_recent)
+    for i in range(n_layers):
+        assert_close(outs[i].cpu().numpy(), ref[i], TOL, f"layer {i} ({'FA' if mask[i] else 'SA'})")
