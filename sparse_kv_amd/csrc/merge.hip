@@ -16,7 +16,7 @@ namespace {
 // loaded together with the split states, so a merge of up to kChunk splits
 // costs one round trip to memory; further splits follow kChunk at a time.
 // A state with l = 0 is empty: it never touches the sums, whatever its o.
-constexpr int kChunk = 16;
+constexpr int kChunk = 32;
 
 template <int PER>
 __device__ __forceinline__ void load_row_part(const float* src, float (&x)[PER]) {
